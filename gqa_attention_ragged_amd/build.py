@@ -1,0 +1,76 @@
+"""Build the HIP library libgqa_attn.so (gfx950) in-tree.
+
+hipcc compiles each source under csrc/ to an object; the objects are linked
+into gqa_attention_ragged_amd/lib/libgqa_attn.so.  The HIP runtime is linked
+by the name "libamdhip64.so", so that inside a PyTorch process the runtime
+PyTorch already loaded is the one the library uses (same streams, same
+allocations); outside PyTorch the loader finds ROCm's own copy.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "lib", "libgqa_attn.so")
+SOURCES = ["gqa_attn.cpp", "prefill.hip", "decode.hip"]
+ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
+    # never let the compiler form packed fp32 VALU ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _hip_runtime_dir() -> str:
+    """Directory holding the libamdhip64.so the library should bind to."""
+    try:
+        import torch  # noqa: F401  (plumbing only: pick the runtime torch loads)
+        d = os.path.join(os.path.dirname(torch.__file__), "lib")
+        if os.path.exists(os.path.join(d, "libamdhip64.so")):
+            return d
+    except Exception:
+        pass
+    return os.path.join(ROCM, "lib")
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = ["hipcc", "-x", "hip", *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"hipcc failed on {src}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    rt = _hip_runtime_dir()
+    tmp = LIB + ".tmp%d" % os.getpid()
+    # plain g++ link: hipcc would add its own -lamdhip64 (soname libamdhip64.so.7)
+    cmd = ["g++", "-shared", "-fPIC", *objs, "-o", tmp, "-L", rt, "-l:libamdhip64.so",
+           f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}", "-Wl,--no-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

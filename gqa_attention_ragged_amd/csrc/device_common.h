@@ -1,0 +1,130 @@
+// device_common.h -- gfx950 building blocks shared by the attention kernels:
+// vector types, MFMA wrappers, E4M3FN conversions and the parameter blocks
+// the host passes to each kernel.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+struct fp8 { uint8_t bits; };  // OCP E4M3FN storage
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- parameters
+// Element strides of a [rows, heads, D] view of a Q / K / V / Y tensor: row
+// (b, h, i) lives at  base + rowbase(b) + h * sh + i * sn  where rowbase is
+// b * sb for the padded form and cum[b] * sn for the packed form.
+struct TensorView {
+    const void* ptr;
+    int64_t sb, sh, sn;
+};
+
+enum MaskKind { MASK_NONE = 0, MASK_BOOL = 1, MASK_F16 = 2, MASK_BF16 = 3, MASK_F32 = 4 };
+
+struct AttnParams {
+    TensorView q, k, v;
+    void* out;
+    int64_t o_sb, o_sh, o_sn;
+    const void* mask;
+    int64_t m_sb, m_sh, m_si, m_sj;  // 0 on broadcast dimensions
+    int32_t mask_kind;
+    int32_t mask_vec;                 // 1 if 4-key groups of the mask are aligned & contiguous
+    const int32_t* ql;                // cumulative query lengths or null
+    const int32_t* kl;                // cumulative (packed KV) / per-batch (padded) / null
+    int32_t q_packed, kv_packed;
+    int32_t batch, n_q, n_kv;         // n_q / n_kv: padded extents
+    int32_t causal;                   // 0 none, 1 upper_left, 2 lower_right
+    int32_t norm_none;                // 1: TRT_normalization_op "none"
+    int32_t qdq;                      // 0 off, 1 fp8, 2 int8
+    float scale, qscale, k_descale, v_descale;
+    int32_t hq, hkv, group;           // group = hq / hkv
+    int32_t heads_per_wg, rows_per_wg;
+    // decode split-KV
+    float* part_o;                    // [B, Hq, S, D]
+    float* part_ml;                   // [B, Hq, S, 2]
+    int32_t split_keys, n_splits;
+};
+
+// ---------------------------------------------------------------- lengths
+__device__ __forceinline__ int q_len_of(const AttnParams& p, int b) {
+    return p.ql ? (p.ql[b + 1] - p.ql[b]) : p.n_q;
+}
+__device__ __forceinline__ int kv_len_of(const AttnParams& p, int b) {
+    if (p.kv_packed) return p.kl[b + 1] - p.kl[b];
+    return p.kl ? p.kl[b] : p.n_kv;
+}
+__device__ __forceinline__ int64_t q_rowbase(const AttnParams& p, int b) {
+    return p.q_packed ? (int64_t)p.ql[b] * p.q.sn : (int64_t)b * p.q.sb;
+}
+__device__ __forceinline__ int64_t o_rowbase(const AttnParams& p, int b) {
+    return p.q_packed ? (int64_t)p.ql[b] * p.o_sn : (int64_t)b * p.o_sb;
+}
+__device__ __forceinline__ int64_t kv_rowbase(const AttnParams& p, const TensorView& t, int b) {
+    return p.kv_packed ? (int64_t)p.kl[b] * t.sn : (int64_t)b * t.sb;
+}
+
+// ---------------------------------------------------------------- MFMA
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32x64, both operands E4M3FN, no block scaling.
+__device__ __forceinline__ f32x16 mfma32_fp8(i32x8 a, i32x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<f16> { typedef f16x8 type; };
+template <> struct Vec8<bf16> { typedef bf16x8 type; };
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ f16 to_t(float x, f16*) { return (f16)x; }
+__device__ __forceinline__ bf16 to_t(float x, bf16*) { return (bf16)x; }
+
+// Round |x| <= 448 to the nearest E4M3FN code (ties to even).  The hardware
+// conversion rounds to nearest-even but does not saturate, so the input is
+// clamped to the format's range first (saturating reading of Q/DQ).
+__device__ __forceinline__ uint32_t f32_to_e4m3_pair(float a, float b) {
+    a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+    b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+template <int BYTE>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
+}
+
+// Eight E4M3FN codes (two dwords) -> eight 16-bit values (exact: every
+// E4M3FN value is representable in f16 and bf16).
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type e4m3x8_to(u32x2 w) {
+    typename Vec8<T>::type r;
+    r[0] = (T)e4m3_to_f32<0>(w[0]); r[1] = (T)e4m3_to_f32<1>(w[0]);
+    r[2] = (T)e4m3_to_f32<2>(w[0]); r[3] = (T)e4m3_to_f32<3>(w[0]);
+    r[4] = (T)e4m3_to_f32<0>(w[1]); r[5] = (T)e4m3_to_f32<1>(w[1]);
+    r[6] = (T)e4m3_to_f32<2>(w[1]); r[7] = (T)e4m3_to_f32<3>(w[1]);
+    return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace gqa

@@ -1,0 +1,339 @@
+// gqa_attn.cpp -- host side of the C ABI declared in include/gqa_attn.h:
+// argument validation, kernel selection, launch geometry, launches.
+//
+// The host never reads device memory: every geometry decision uses shapes
+// only (T, B, N, H), and the kernels resolve the ragged lengths themselves.
+#include "gqa_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[256];
+thread_local int g_hip_err = 0;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int elem_bytes(int dt) {
+    switch (dt) {
+    case GQA_DT_F16:
+    case GQA_DT_BF16: return 2;
+    case GQA_DT_FP8_E4M3: return 1;
+    case GQA_DT_F32: return 4;
+    case GQA_DT_BOOL: return 1;
+    }
+    return 0;
+}
+
+int elem_kind(int dt) {
+    return dt == GQA_DT_F16 ? gqa::ELEM_F16 : dt == GQA_DT_BF16 ? gqa::ELEM_BF16 : gqa::ELEM_FP8;
+}
+
+int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
+
+enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2 };
+
+struct Plan {
+    Kernel kernel = K_NONE;
+    gqa::AttnParams p{};
+    int q_elem = 0, kv_elem = 0, head_dim = 0;
+    int grid_x = 0, grid_y = 0;
+    size_t workspace = 0;
+};
+
+// Checks that a Q/K/V/Y tensor has the rank of its form and a contiguous,
+// suitably aligned head_size dimension.
+int check_tensor(const gqa_tensor_t& t, const char* name, int form) {
+    if (!t.data) return fail(GQA_ERR_INVALID_ARG, "%s: null data pointer", name);
+    const int want = form == GQA_FORM_PACKED_NHD ? 3 : 4;
+    if (t.ndim != want)
+        return fail(GQA_ERR_INVALID_ARG, "%s: rank %d, the %s form needs rank %d", name, t.ndim,
+                    form == GQA_FORM_PACKED_NHD ? "packed_nhd" : "padded_bhnd", want);
+    for (int d = 0; d < t.ndim; ++d)
+        if (t.shape[d] < 0) return fail(GQA_ERR_INVALID_ARG, "%s: negative extent", name);
+    if (t.stride[t.ndim - 1] != 1)
+        return fail(GQA_ERR_INVALID_ARG, "%s: head_size dimension must be contiguous", name);
+    const int es = elem_bytes(t.dtype);
+    if (es == 0) return fail(GQA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, t.dtype);
+    const int64_t align_elems = 16 / es;
+    if ((uintptr_t)t.data % 16)
+        return fail(GQA_ERR_UNSUPPORTED, "%s: data pointer must be 16-byte aligned", name);
+    for (int d = 0; d + 1 < t.ndim; ++d)
+        if (t.stride[d] % align_elems)
+            return fail(GQA_ERR_UNSUPPORTED, "%s: stride %d (%lld) must be a multiple of 16 bytes",
+                        name, d, (long long)t.stride[d]);
+    return GQA_OK;
+}
+
+int plan_call(const gqa_attn_args_t* a, Plan* plan) {
+    if (!a) return fail(GQA_ERR_INVALID_ARG, "args is null");
+    const int qf = a->query_form, kf = a->kv_form;
+    if ((qf != 0 && qf != 1) || (kf != 0 && kf != 1))
+        return fail(GQA_ERR_INVALID_ARG, "query_form / kv_form must be 0 or 1");
+    if (a->causal_kind < 0 || a->causal_kind > 2)
+        return fail(GQA_ERR_INVALID_ARG, "causal_kind must be 0, 1 or 2");
+    if (a->norm != GQA_NORM_SOFTMAX && a->norm != GQA_NORM_NONE)
+        return fail(GQA_ERR_INVALID_ARG, "norm must be softmax or none");
+    if (a->qdq < 0 || a->qdq > 2) return fail(GQA_ERR_INVALID_ARG, "qdq must be 0, 1 or 2");
+
+    int st;
+    if ((st = check_tensor(a->q, "q", qf))) return st;
+    if ((st = check_tensor(a->k, "k", kf))) return st;
+    if ((st = check_tensor(a->v, "v", kf))) return st;
+    if ((st = check_tensor(a->out, "out", qf))) return st;
+
+    const int qdt = a->q.dtype, kdt = a->k.dtype;
+    if (qdt != GQA_DT_F16 && qdt != GQA_DT_BF16 && qdt != GQA_DT_FP8_E4M3)
+        return fail(GQA_ERR_INVALID_ARG, "q dtype must be f16, bf16 or fp8 e4m3");
+    if (a->v.dtype != kdt) return fail(GQA_ERR_INVALID_ARG, "k and v dtypes differ");
+    const bool kv_cache8 = kdt == GQA_DT_FP8_E4M3 && qdt != GQA_DT_FP8_E4M3;
+    if (kdt != qdt && !kv_cache8)
+        return fail(GQA_ERR_INVALID_ARG, "k/v dtype must equal q's, or be fp8 with 16-bit q");
+    const int out_dt = qdt == GQA_DT_FP8_E4M3 ? GQA_DT_F16 : qdt;
+    if (a->out.dtype != out_dt)
+        return fail(GQA_ERR_INVALID_ARG, "out dtype must be %s",
+                    out_dt == GQA_DT_F16 ? "f16" : "bf16");
+
+    const int qn = a->q.ndim, kn = a->k.ndim;
+    const int64_t D = a->q.shape[qn - 1];
+    if (a->k.shape[kn - 1] != D || a->v.shape[kn - 1] != D)
+        return fail(GQA_ERR_INVALID_ARG, "head_size of q, k and v differ");
+    for (int d = 0; d < qn; ++d)
+        if (a->out.shape[d] != a->q.shape[d])
+            return fail(GQA_ERR_INVALID_ARG, "out shape must equal q's shape");
+    const int64_t Hq = a->q.shape[1], Hkv = a->k.shape[1];
+    if (a->num_heads != Hq) return fail(GQA_ERR_INVALID_ARG, "num_heads != q's head dimension");
+    if (a->kv_num_heads != Hkv || a->v.shape[1] != Hkv)
+        return fail(GQA_ERR_INVALID_ARG, "kv_num_heads != k/v head dimension");
+    if (Hq <= 0 || Hkv <= 0 || Hq % Hkv)
+        return fail(GQA_ERR_INVALID_ARG, "num_heads must be a positive multiple of kv_num_heads");
+    for (int d = 0; d < kn; ++d)
+        if (a->v.shape[d] != a->k.shape[d]) return fail(GQA_ERR_INVALID_ARG, "k and v shapes differ");
+
+    const int64_t B = a->batch;
+    if (B < 0) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0");
+    if (qf == GQA_FORM_PADDED_BHND && a->q.shape[0] != B)
+        return fail(GQA_ERR_INVALID_ARG, "batch != q.shape[0]");
+    if (kf == GQA_FORM_PADDED_BHND && a->k.shape[0] != B)
+        return fail(GQA_ERR_INVALID_ARG, "batch != k.shape[0]");
+    if (qf == GQA_FORM_PACKED_NHD && !a->query_lengths)
+        return fail(GQA_ERR_INVALID_ARG, "query_lengths is required for packed_nhd Q");
+    if (kf == GQA_FORM_PACKED_NHD && !a->kv_lengths)
+        return fail(GQA_ERR_INVALID_ARG, "kv_lengths is required for packed_nhd KV");
+
+    const int64_t Nq = qf == GQA_FORM_PADDED_BHND ? a->q.shape[2] : 0;
+    const int64_t Nkv = kf == GQA_FORM_PADDED_BHND ? a->k.shape[2] : 0;
+    const int64_t Tq = qf == GQA_FORM_PACKED_NHD ? a->q.shape[0] : 0;
+    const int64_t Tkv = kf == GQA_FORM_PACKED_NHD ? a->k.shape[0] : 0;
+    const int64_t kv_max = kf == GQA_FORM_PADDED_BHND ? Nkv : Tkv;
+    if (Nq > INT32_MAX || Nkv > INT32_MAX || Tq > INT32_MAX || Tkv > INT32_MAX || B > 65535)
+        return fail(GQA_ERR_UNSUPPORTED, "extents beyond the int32 / grid limits of this build");
+
+    if (a->qdq != GQA_QDQ_OFF && !(a->qscale > 0.f && std::isfinite(a->qscale)))
+        return fail(GQA_ERR_INVALID_ARG, "qscale must be finite and > 0 when qdq is on");
+    if (!std::isfinite(a->scale) || !std::isfinite(a->k_descale) || !std::isfinite(a->v_descale))
+        return fail(GQA_ERR_INVALID_ARG, "scale / descales must be finite");
+
+    // mask
+    gqa::AttnParams& p = plan->p;
+    p = gqa::AttnParams{};
+    p.mask_kind = gqa::MASK_NONE;
+    const gqa_tensor_t& m = a->attn_mask;
+    if (m.data) {
+        if (m.ndim < 1 || m.ndim > 4) return fail(GQA_ERR_INVALID_ARG, "attn_mask rank must be 1..4");
+        switch (m.dtype) {
+        case GQA_DT_BOOL: p.mask_kind = gqa::MASK_BOOL; break;
+        case GQA_DT_F16: p.mask_kind = gqa::MASK_F16; break;
+        case GQA_DT_BF16: p.mask_kind = gqa::MASK_BF16; break;
+        case GQA_DT_F32: p.mask_kind = gqa::MASK_F32; break;
+        default: return fail(GQA_ERR_INVALID_ARG, "attn_mask dtype must be bool, f16, bf16 or f32");
+        }
+        int64_t ext[4] = {1, 1, 1, 1}, str[4] = {0, 0, 0, 0};
+        for (int d = 0; d < m.ndim; ++d) {
+            ext[4 - m.ndim + d] = m.shape[d];
+            str[4 - m.ndim + d] = m.shape[d] == 1 ? 0 : m.stride[d];
+            if (m.shape[d] < 1) return fail(GQA_ERR_INVALID_ARG, "attn_mask has an empty dimension");
+        }
+        if (ext[0] != 1 && ext[0] != B) return fail(GQA_ERR_INVALID_ARG, "attn_mask batch extent");
+        if (ext[1] != 1 && ext[1] != Hq) return fail(GQA_ERR_INVALID_ARG, "attn_mask head extent");
+        if (qf == GQA_FORM_PADDED_BHND && !a->query_lengths && ext[2] != 1 && ext[2] < Nq)
+            return fail(GQA_ERR_INVALID_ARG, "attn_mask query extent < N_q");
+        if (kf == GQA_FORM_PADDED_BHND && !a->kv_lengths && ext[3] != 1 && ext[3] < Nkv)
+            return fail(GQA_ERR_INVALID_ARG, "attn_mask key extent < N_kv");
+        p.mask = m.data;
+        p.m_sb = str[0];
+        p.m_sh = str[1];
+        p.m_si = str[2];
+        p.m_sj = str[3];
+        const int mes = elem_bytes(m.dtype);
+        p.mask_vec = str[3] == 1 && ((uintptr_t)m.data % (4 * mes)) == 0 && str[0] % 4 == 0 &&
+                     str[1] % 4 == 0 && str[2] % 4 == 0;
+    }
+
+    // supported combinations
+    if (D != 64 && D != 128) return fail(GQA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+    if (qdt == GQA_DT_FP8_E4M3 && a->qdq != GQA_QDQ_FP8_E4M3)
+        return fail(GQA_ERR_UNSUPPORTED, "fp8 Q/K/V needs fp8 Q/DQ of the scores");
+    const int64_t G = Hq / Hkv;
+    const bool decode = qf == GQA_FORM_PADDED_BHND && Nq == 1 && !m.data &&
+                        a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
+                        a->causal_kind != GQA_CAUSAL_UPPER_LEFT && G <= 16 &&
+                        qdt != GQA_DT_FP8_E4M3;
+    if (kv_cache8 && !decode)
+        return fail(GQA_ERR_UNSUPPORTED,
+                    "an fp8 KV cache with 16-bit Q is supported for the decode step "
+                    "(padded Q with N_q = 1, softmax, no mask, no Q/DQ, causal none/lower_right)");
+
+    // common parameters
+    auto view = [](const gqa_tensor_t& t, int form) {
+        gqa::TensorView v;
+        v.ptr = t.data;
+        if (form == GQA_FORM_PACKED_NHD) {
+            v.sb = 0;
+            v.sh = t.stride[1];
+            v.sn = t.stride[0];
+        } else {
+            v.sb = t.stride[0];
+            v.sh = t.stride[1];
+            v.sn = t.stride[2];
+        }
+        return v;
+    };
+    p.q = view(a->q, qf);
+    p.k = view(a->k, kf);
+    p.v = view(a->v, kf);
+    const gqa::TensorView ov = view(a->out, qf);
+    p.out = a->out.data;
+    p.o_sb = ov.sb;
+    p.o_sh = ov.sh;
+    p.o_sn = ov.sn;
+    p.ql = a->query_lengths;
+    p.kl = a->kv_lengths;
+    p.q_packed = qf;
+    p.kv_packed = kf;
+    p.batch = (int)B;
+    p.n_q = (int)Nq;
+    p.n_kv = (int)Nkv;
+    p.causal = a->causal_kind;
+    p.norm_none = a->norm == GQA_NORM_NONE;
+    p.qdq = a->qdq;
+    p.scale = a->scale;
+    p.qscale = a->qdq ? a->qscale : 1.f;
+    p.k_descale = a->k_descale;
+    p.v_descale = a->v_descale;
+    p.hq = (int)Hq;
+    p.hkv = (int)Hkv;
+    p.group = (int)G;
+    plan->q_elem = elem_kind(qdt);
+    plan->kv_elem = elem_kind(kdt);
+    plan->head_dim = (int)D;
+
+    // nothing to compute
+    if (B == 0 || (qf == GQA_FORM_PADDED_BHND && Nq == 0) ||
+        (qf == GQA_FORM_PACKED_NHD && Tq == 0)) {
+        plan->kernel = K_NONE;
+        plan->workspace = 0;
+        return GQA_OK;
+    }
+
+    if (decode) {
+        int C = 1024;
+        auto nsplit = [&](int c) { return (kv_max + c - 1) / c; };
+        while (C > 128 && B * Hkv * nsplit(C) < 4096) C /= 2;
+        const int64_t S = kv_max > 0 ? nsplit(C) : 1;
+        if (S > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many KV splits");
+        p.split_keys = C;
+        p.n_splits = (int)S;
+        plan->kernel = K_DECODE;
+        plan->workspace = (size_t)B * Hq * S * (D + 2) * sizeof(float) + 256;
+        return GQA_OK;
+    }
+
+    const int hw = gcd((int)G, 4);
+    const int R = 32 * (4 / hw);
+    p.heads_per_wg = hw;
+    p.rows_per_wg = R;
+    int64_t gx = qf == GQA_FORM_PADDED_BHND ? B * ((Nq + R - 1) / R) : (Tq + R - 1) / R + B;
+    if (gx > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many query tiles");
+    plan->grid_x = (int)gx;
+    plan->grid_y = (int)(Hq / hw);
+    if (plan->grid_y > 65535) return fail(GQA_ERR_UNSUPPORTED, "too many heads");
+    plan->kernel = K_PREFILL;
+    plan->workspace = 0;
+    return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gqa_attn_validate(const gqa_attn_args_t* args) {
+    Plan plan;
+    return plan_call(args, &plan);
+}
+
+int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes) {
+    Plan plan;
+    const int st = plan_call(args, &plan);
+    if (st == GQA_OK && bytes) *bytes = plan.workspace;
+    return st;
+}
+
+int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    Plan plan;
+    int st = plan_call(args, &plan);
+    if (st != GQA_OK) return st;
+    if (plan.kernel == K_NONE) return GQA_OK;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipSuccess;
+    if (plan.kernel == K_DECODE) {
+        if (!workspace || workspace_bytes < plan.workspace)
+            return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed", plan.workspace);
+        uintptr_t w = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+        const int64_t slots = (int64_t)plan.p.batch * plan.p.hq * plan.p.n_splits;
+        plan.p.part_o = (float*)w;
+        plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
+        e = gqa::launch_decode(plan.p, plan.q_elem, plan.kv_elem, plan.head_dim, s);
+    } else {
+        e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
+    }
+    if (e != hipSuccess) {
+        g_hip_err = (int)e;
+        return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return GQA_OK;
+}
+
+const char* gqa_attn_status_str(int status) {
+    switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported combination";
+    case GQA_ERR_WORKSPACE: return "workspace too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* gqa_attn_last_error(void) { return g_err; }
+
+int gqa_attn_last_hip_error(void) { return g_hip_err; }
+
+int gqa_attn_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,618 @@
+// prefill.hip -- fused ragged GQA attention for query tiles (prefill, chunked
+// context, and any query length), gfx950.
+//
+// Computes, per valid query row, BMM1 -> causal / length / mask predicate ->
+// normalization (softmax or none) -> optional quantize-dequantize of the
+// normalized scores -> BMM2, as the onnx-tensorrt "TensorRT Custom Operator
+// Schemas" page defines TRT_Attention and TRT_QuantizedAttention.
+//
+// Work decomposition
+//   * A workgroup is 4 waves.  Each wave owns 32 query rows of one query
+//     head.  The waves of a workgroup share one KV head: with group size
+//     G = H_q / H_kv they cover HW = gcd(G, 4) heads of the same KV group and
+//     4 / HW blocks of 32 rows, so every K/V tile staged in LDS feeds 4 waves.
+//   * blockIdx.x enumerates query-row tiles over the whole ragged batch
+//     (sum_b ceil(q_len_b / rows_per_wg)); the tile -> (b, tile) map is
+//     rebuilt on the device from the cumulative lengths, so the host never
+//     reads device memory.  blockIdx.y enumerates head groups.
+//   * The key loop streams 64-key tiles through double-buffered LDS: K
+//     row-major, V transposed (V^T[d][key]) so that both MFMA operands are
+//     read with 16-byte LDS loads.
+//   * Scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles, so
+//     each lane owns one query row (lane % 32) and 16 of every 32 keys; the
+//     row max / sum need one exchange with lane ^ 32 only.  O is likewise
+//     accumulated transposed, O^T = V^T P^T.
+//   * Softmax runs online in the exp2 domain (scale * log2 e folded into the
+//     score scale), the published online-normalizer method (Milakov &
+//     Gimelshein 2018, as used by FlashAttention-2).  With Q/DQ the
+//     normalized P needs the final row max and sum, so a first pass over the
+//     keys computes them and a second pass quantizes exactly.
+//   * Padding is never read (loads are predicated on the valid lengths) and
+//     output rows are only written when they are valid.
+#include "device_common.h"
+#include "launch.h"
+
+#include <type_traits>
+
+namespace gqa {
+
+template <typename TI, int D>
+struct Cfg {
+    static constexpr bool FP8 = std::is_same<TI, fp8>::value;
+    static constexpr int ES = FP8 ? 1 : 2;          // element bytes
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int KROW = D * ES + 16;        // LDS bytes per K row (padded)
+    static constexpr int VROW = BN * ES + 16;       // LDS bytes per V^T row (padded)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int VBYTES = D * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int CHUNKS = D / 8;            // 8-element chunks per row
+    static constexpr int KPT = D / 32;              // keys per loader thread
+    static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
+};
+
+// Position of key o (0..63 within a tile) inside an LDS V^T row, chosen so
+// that the lane group g of a BMM2 A-operand read sees, in register order,
+// exactly the keys whose probabilities the same lane group holds in its
+// S^T accumulator (see the PV step).  A bit permutation of o.
+template <bool FP8>
+__device__ __forceinline__ int vpos(int o) {
+    if (FP8) return ((o & 7) >> 2) * 32 + (o >> 5) * 16 + ((o & 31) >> 3) * 4 + (o & 3);
+    return (o >> 4) * 16 + ((o & 7) >> 2) * 8 + ((o & 15) >> 3) * 4 + (o & 3);
+}
+
+template <typename TI>
+struct Chunk { typedef u32x4 type; };  // 8 x 16-bit
+template <>
+struct Chunk<fp8> { typedef u32x2 type; };  // 8 x 8-bit
+
+// Element e of an 8-element chunk, as raw bits.
+__device__ __forceinline__ uint32_t chunk_elem(u32x4 c, int e) {
+    return (c[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+}
+__device__ __forceinline__ uint32_t chunk_elem(u32x2 c, int e) {
+    return (c[e >> 2] >> ((e & 3) * 8)) & 0xffu;
+}
+
+// ------------------------------------------------------------------ mask
+struct MaskGroup {
+    float add[4];
+    bool ok[4];
+};
+
+__device__ __forceinline__ float mask_scalar(const AttnParams& p, const char* row, int64_t j) {
+    switch (p.mask_kind) {
+    case MASK_BOOL: return ((const uint8_t*)row)[j * p.m_sj] ? 1.f : 0.f;
+    case MASK_F16: return (float)((const f16*)row)[j * p.m_sj];
+    case MASK_BF16: return (float)((const bf16*)row)[j * p.m_sj];
+    default: return ((const float*)row)[j * p.m_sj];
+    }
+}
+
+// Mask values for keys jg..jg+3 of one row; keys >= kv_len are not read.
+__device__ __forceinline__ MaskGroup load_mask_group(const AttnParams& p, const char* row, int jg,
+                                                     int kv_len) {
+    MaskGroup m;
+    const bool is_bool = p.mask_kind == MASK_BOOL;
+    if (p.mask_vec && jg + 3 < kv_len) {
+        if (is_bool) {
+            uint32_t w = *(const uint32_t*)(row + (int64_t)jg);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { m.ok[u] = (w >> (8 * u)) & 0xff; m.add[u] = 0.f; }
+        } else if (p.mask_kind == MASK_F32) {
+            f32x4 w = *(const f32x4*)(row + (int64_t)jg * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { m.add[u] = w[u]; m.ok[u] = true; }
+        } else {
+            u32x2 w = *(const u32x2*)(row + (int64_t)jg * 2);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t h = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
+                if (p.mask_kind == MASK_F16) {
+                    m.add[u] = (float)__builtin_bit_cast(f16, (uint16_t)h);
+                } else {
+                    m.add[u] = __builtin_bit_cast(float, h << 16);
+                }
+                m.ok[u] = true;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m.add[u] = 0.f;
+            m.ok[u] = false;
+            if (jg + u < kv_len) {
+                float x = mask_scalar(p, row, jg + u);
+                if (is_bool) m.ok[u] = x != 0.f;
+                else { m.add[u] = x; m.ok[u] = true; }
+            }
+        }
+    }
+    return m;
+}
+
+// ------------------------------------------------------------------ kernel
+enum PassKind { PASS_STATS = 0, PASS_ONLINE = 1, PASS_FIXED = 2, PASS_NONE = 3 };
+
+template <typename TI, int D>
+struct Prefill {
+    typedef Cfg<TI, D> C;
+    typedef typename Chunk<TI>::type ChunkT;
+    // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
+    typedef typename std::conditional<C::FP8, f16, TI>::type T16;
+    typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
+
+    // Per-workgroup state shared by the passes.
+    struct Ctx {
+        int b, q_len, kv_len, diag, ntiles;
+        int wr0;              // first row of this wave
+        bool wave_rows;       // wave has at least one valid row
+        int wave_kv_end;      // keys this wave can see (causal)
+        const char* kbase;    // K rows of (b, kv head)
+        const char* vbase;
+        const char* mrow;     // mask row of this lane's query row (or null)
+        int i;                // this lane's query row
+    };
+
+    __device__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
+                                     ChunkT (&rk)[C::KPT], ChunkT (&rv)[C::KPT]) {
+        const int t = threadIdx.x;
+        const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
+#pragma unroll
+        for (int kk = 0; kk < C::KPT; ++kk) {
+            const int j = tile * C::BN + kg * C::KPT + kk;
+            rk[kk] = ChunkT{};
+            rv[kk] = ChunkT{};
+            if (j < c.kv_len) {
+                rk[kk] = *(const ChunkT*)(c.kbase + ((int64_t)j * p.k.sn + ch * 8) * C::ES);
+                if (with_v)
+                    rv[kk] = *(const ChunkT*)(c.vbase + ((int64_t)j * p.v.sn + ch * 8) * C::ES);
+            }
+        }
+    }
+
+    __device__ static void store_tile(char* stage, bool with_v, const ChunkT (&rk)[C::KPT],
+                                      const ChunkT (&rv)[C::KPT]) {
+        const int t = threadIdx.x;
+        const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
+        char* sK = stage;
+        char* sV = stage + C::KBYTES;
+#pragma unroll
+        for (int kk = 0; kk < C::KPT; ++kk)
+            *(ChunkT*)(sK + (kg * C::KPT + kk) * C::KROW + ch * 8 * C::ES) = rk[kk];
+        if (!with_v) return;
+        const int pos = vpos<C::FP8>(kg * C::KPT);  // KPT consecutive keys -> contiguous
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = ch * 8 + e;
+            char* dst = sV + d * C::VROW + pos * C::ES;
+            if (C::FP8) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int kk = 0; kk < C::KPT; ++kk) w |= chunk_elem(rv[kk], e) << (8 * kk);
+                if (C::KPT == 4) *(uint32_t*)dst = w;
+                else if (C::KPT == 2) *(uint16_t*)dst = (uint16_t)w;
+                else *(uint8_t*)dst = (uint8_t)w;
+            } else {
+                if (C::KPT == 4) {
+                    u32x2 w;
+                    w[0] = chunk_elem(rv[0], e) | (chunk_elem(rv[1], e) << 16);
+                    w[1] = chunk_elem(rv[2 % C::KPT], e) | (chunk_elem(rv[3 % C::KPT], e) << 16);
+                    *(u32x2*)dst = w;
+                } else {
+                    *(uint32_t*)dst = chunk_elem(rv[0], e) | (chunk_elem(rv[1 % C::KPT], e) << 16);
+                }
+            }
+        }
+    }
+
+    // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.
+    __device__ static void bmm1(const char* sK, const void* qreg, f32x16 (&s)[2]) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 acc = {};
+            const char* row = sK + (kb * 32 + lr) * C::KROW;
+            if (C::FP8) {
+                const i32x8* q8 = (const i32x8*)qreg;
+#pragma unroll
+                for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                    const u32x4* src = (const u32x4*)(row + ks * 64 + lg * 32);
+                    u32x4 lo = src[0], hi = src[1];
+                    i32x8 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                    acc = mfma32_fp8(a, q8[ks], acc);
+                }
+            } else {
+                typedef typename Vec8<T16>::type V8;
+                const V8* q16 = (const V8*)qreg;
+#pragma unroll
+                for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                    V8 a = *(const V8*)(row + (ks * 16 + lg * 8) * 2);
+                    acc = mfma32(a, q16[ks], acc);
+                }
+            }
+            s[kb] = acc;
+        }
+    }
+
+    // Scale the raw scores and apply the causal / length / mask predicate.
+    // Disallowed entries become -inf (softmax) or are flagged via 0 (none).
+    __device__ static void predicate(const AttnParams& p, const Ctx& c, int tile, f32x16 (&s)[2],
+                                     float sc, float ac, bool none_norm) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+        const int j0 = tile * C::BN;
+        const bool row_ok = c.i < c.q_len;
+        const bool full_rows = c.wr0 + 32 <= c.q_len;
+        const bool need = p.mask_kind != MASK_NONE || j0 + C::BN > c.kv_len || !full_rows ||
+                          (p.causal && j0 + C::BN - 1 > c.wr0 + c.diag);
+        const float off = none_norm ? 0.f : -INFINITY;
+        if (!need) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kb][r] *= sc;
+            return;
+        }
+        (void)lr;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
+                MaskGroup mg;
+                if (p.mask_kind != MASK_NONE && row_ok) {
+                    mg = load_mask_group(p, c.mrow, jg, c.kv_len);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { mg.add[u] = 0.f; mg.ok[u] = true; }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = jg + u;
+                    const int r = rq * 4 + u;
+                    bool a = row_ok && j < c.kv_len && (p.causal == 0 || j <= c.i + c.diag);
+                    float v = s[kb][r] * sc;
+                    if (p.mask_kind == MASK_BOOL) {
+                        a = a && mg.ok[u];
+                    } else if (p.mask_kind != MASK_NONE) {
+                        a = a && !(__builtin_isinf(mg.add[u]) && mg.add[u] < 0.f);
+                        v += mg.add[u] * ac;
+                    }
+                    s[kb][r] = a ? v : off;
+                }
+            }
+        }
+    }
+
+    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile.
+    __device__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], f32x16* o) {
+        typedef typename Vec8<T16>::type V8;
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            V8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                V8 a = *(const V8*)(sV + (db * 32 + lr) * C::VROW + (ks * 16 + lg * 8) * 2);
+                o[db] = mfma32(a, b, o[db]);
+            }
+        }
+    }
+
+    // "none" normalization keeps unbounded scores: split each into a 16-bit
+    // high part and a 16-bit remainder so BMM2 keeps ~fp32 accuracy.
+    __device__ static void bmm2_16_split(const char* sV, const f32x16 (&pv)[2], f32x16* o) {
+        typedef typename Vec8<T16>::type V8;
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            V8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = pv[ks >> 1][(ks & 1) * 8 + e];
+                T16 h = to_t(x, (T16*)nullptr);
+                bh[e] = h;
+                bl[e] = to_t(x - (float)h, (T16*)nullptr);
+            }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                V8 a = *(const V8*)(sV + (db * 32 + lr) * C::VROW + (ks * 16 + lg * 8) * 2);
+                o[db] = mfma32(a, bh, o[db]);
+                o[db] = mfma32(a, bl, o[db]);
+            }
+        }
+    }
+
+    // fp8 BMM2: P' codes (E4M3FN) against V^T codes, one 64-key k-step.
+    __device__ static void bmm2_fp8(const char* sV, const i32x8& codes, f32x16* o) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const u32x4* src = (const u32x4*)(sV + (db * 32 + lr) * C::VROW + lg * 32);
+            u32x4 lo = src[0], hi = src[1];
+            i32x8 a;
+            a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+            a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+            o[db] = mfma32_fp8(a, codes, o[db]);
+        }
+    }
+
+    // Quantize x (= P / qscale) and return the dequantized code value
+    // (without the qscale factor, which the epilogue applies).
+    __device__ static float qdq_value(float x, int kind) {
+        if (kind == 1) {
+            uint32_t code = f32_to_e4m3_pair(x, 0.f);
+            return e4m3_to_f32<0>(code);
+        }
+        float r = __builtin_rintf(x);
+        return __builtin_amdgcn_fmed3f(r, -128.f, 127.f);
+    }
+
+    // One sweep over the key tiles of this workgroup.
+    template <int KIND>
+    __device__ static void sweep(const AttnParams& p, const Ctx& c, char* smem, const void* qreg,
+                                 float sc, float ac, float& m_run, float& l_run, float inv,
+                                 f32x16* o) {
+        const bool with_v = KIND != PASS_STATS;
+        ChunkT rk[C::KPT], rv[C::KPT];
+        if (c.ntiles > 0) {
+            load_tile(p, c, 0, with_v, rk, rv);
+            store_tile(smem, with_v, rk, rv);
+        }
+        __syncthreads();
+        for (int it = 0; it < c.ntiles; ++it) {
+            const bool more = it + 1 < c.ntiles;
+            if (more) load_tile(p, c, it + 1, with_v, rk, rv);
+            char* stage = smem + (it & 1) * C::STAGE;
+            const int j0 = it * C::BN;
+            if (c.wave_rows && j0 < c.wave_kv_end) {
+                f32x16 s[2];
+                bmm1(stage, qreg, s);
+                predicate(p, c, it, s, sc, ac, KIND == PASS_NONE);
+                if (KIND == PASS_NONE) {
+                    if (p.qdq) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) s[kb][r] = qdq_value(s[kb][r] * inv, p.qdq);
+                        if (C::FP8) {
+                            i32x8 codes;
+#pragma unroll
+                            for (int w = 0; w < 8; ++w) {
+                                const int kb = w >> 2, r0 = (w & 3) * 4;
+                                uint32_t lo = f32_to_e4m3_pair(s[kb][r0], s[kb][r0 + 1]);
+                                uint32_t hi = f32_to_e4m3_pair(s[kb][r0 + 2], s[kb][r0 + 3]);
+                                codes[w] = (int)(lo | (hi << 16));
+                            }
+                            bmm2_fp8(stage + C::KBYTES, codes, o);
+                        } else {
+                            bmm2_16(stage + C::KBYTES, s, o);
+                        }
+                    } else {
+                        bmm2_16_split(stage + C::KBYTES, s, o);
+                    }
+                } else {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                    if (KIND != PASS_FIXED) {
+                        mx = fmaxf(mx, __shfl_xor(mx, 32));
+                        const float m_new = fmaxf(m_run, mx);
+                        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                        const float alpha = fast_exp2(m_run - m_use);
+                        float ls = 0.f;
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const float e = fast_exp2(s[kb][r] - m_use);
+                                s[kb][r] = e;
+                                ls += e;
+                            }
+                        l_run = l_run * alpha + ls;
+                        m_run = m_new;
+                        if (KIND == PASS_ONLINE) {
+#pragma unroll
+                            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                            bmm2_16(stage + C::KBYTES, s, o);
+                        }
+                    } else {
+                        // final max known: P = exp2(s - m) / l, x = P / qscale
+                        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+                        if (C::FP8) {
+                            i32x8 codes;
+#pragma unroll
+                            for (int w = 0; w < 8; ++w) {
+                                const int kb = w >> 2, r0 = (w & 3) * 4;
+                                float x0 = fast_exp2(s[kb][r0] - m_use) * inv;
+                                float x1 = fast_exp2(s[kb][r0 + 1] - m_use) * inv;
+                                float x2 = fast_exp2(s[kb][r0 + 2] - m_use) * inv;
+                                float x3 = fast_exp2(s[kb][r0 + 3] - m_use) * inv;
+                                uint32_t lo = f32_to_e4m3_pair(x0, x1);
+                                uint32_t hi = f32_to_e4m3_pair(x2, x3);
+                                codes[w] = (int)(lo | (hi << 16));
+                            }
+                            bmm2_fp8(stage + C::KBYTES, codes, o);
+                        } else {
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r)
+                                    s[kb][r] = qdq_value(fast_exp2(s[kb][r] - m_use) * inv, p.qdq);
+                            bmm2_16(stage + C::KBYTES, s, o);
+                        }
+                    }
+                }
+            }
+            if (more) store_tile(smem + ((it + 1) & 1) * C::STAGE, with_v, rk, rv);
+            __syncthreads();
+        }
+    }
+
+    __device__ static void run(const AttnParams& p, char* smem) {
+        __shared__ int s_map[2];
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int lr = lane & 31, lg = lane >> 5;
+        const int R = p.rows_per_wg;
+        const int tile = blockIdx.x;
+
+        // ---- ragged tile map: tile -> (b, row tile within b), on wave 0
+        if (wave == 0) {
+            if (lane == 0) s_map[0] = -1;
+            int acc = 0;
+            for (int base = 0; base < p.batch; base += 64) {
+                const int b = base + lane;
+                int n = 0;
+                if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
+                int incl = n;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    int y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                const int excl = incl - n;
+                if (n > 0 && tile >= acc + excl && tile < acc + incl) {
+                    s_map[0] = b;
+                    s_map[1] = tile - acc - excl;
+                }
+                acc += __shfl(incl, 63);
+                if (acc > tile) break;
+            }
+        }
+        __syncthreads();
+        const int b = s_map[0];
+        if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
+
+        Ctx c;
+        c.b = b;
+        c.q_len = q_len_of(p, b);
+        c.kv_len = kv_len_of(p, b);
+        c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
+        const int row0 = s_map[1] * R;
+        const int hw = p.heads_per_wg;
+        const int h = blockIdx.y * hw + (wave % hw);
+        const int kvh = (blockIdx.y * hw) / p.group;
+        c.wr0 = row0 + (wave / hw) * 32;
+        c.i = c.wr0 + lr;
+        c.wave_rows = c.wr0 < c.q_len;
+        const int wg_last = min(row0 + R, c.q_len) - 1;
+        int kv_end = c.kv_len;
+        if (p.causal) kv_end = min(kv_end, wg_last + c.diag + 1);
+        kv_end = max(kv_end, 0);
+        c.ntiles = (kv_end + C::BN - 1) / C::BN;
+        const int wave_last = min(c.wr0 + 32, c.q_len) - 1;
+        c.wave_kv_end = c.kv_len;
+        if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
+        c.kbase = (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * C::ES;
+        c.vbase = (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * C::ES;
+        c.mrow = nullptr;
+        if (p.mask_kind != MASK_NONE) {
+            const int mes = p.mask_kind == MASK_BOOL ? 1 : (p.mask_kind == MASK_F32 ? 4 : 2);
+            c.mrow = (const char*)p.mask +
+                     ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)c.i * p.m_si) * mes;
+        }
+
+        // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg)
+        typedef typename Vec8<T16>::type V8;
+        V8 q16[C::FP8 ? 1 : C::QSTEPS];
+        i32x8 q8[C::FP8 ? C::QSTEPS : 1];
+        {
+            const bool ok = c.i < c.q_len;
+            const char* qrow = (const char*)p.q.ptr +
+                               (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.i * p.q.sn) * C::ES;
+#pragma unroll
+            for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                if (C::FP8) {
+                    u32x4 lo = {}, hi = {};
+                    if (ok) {
+                        const u32x4* src = (const u32x4*)(qrow + ks * 64 + lg * 32);
+                        lo = src[0];
+                        hi = src[1];
+                    }
+                    i32x8 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                    q8[ks % (C::FP8 ? C::QSTEPS : 1)] = a;
+                } else {
+                    V8 a = {};
+                    if (ok) a = *(const V8*)(qrow + (ks * 16 + lg * 8) * 2);
+                    q16[ks % (C::FP8 ? 1 : C::QSTEPS)] = a;
+                }
+            }
+        }
+        const void* qreg = C::FP8 ? (const void*)q8 : (const void*)q16;
+
+        f32x16 o[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.f;
+        const bool none_norm = p.norm_none != 0;
+        const float sc = none_norm ? p.scale * p.k_descale : p.scale * p.k_descale * kLog2e;
+        const float ac = none_norm ? 1.f : kLog2e;
+        float factor = p.v_descale;
+
+        if (none_norm) {
+            const float inv = p.qdq ? 1.f / p.qscale : 1.f;
+            sweep<PASS_NONE>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            if (p.qdq) factor *= p.qscale;
+        } else if (p.qdq) {
+            sweep<PASS_STATS>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
+            sweep<PASS_FIXED>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            factor *= p.qscale;
+        } else {
+            sweep<PASS_ONLINE>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            factor *= l_tot > 0.f ? 1.f / l_tot : 0.f;
+        }
+
+        // ---- epilogue: lane (row lr, group lg) holds O^T[d][row] for
+        // d = db*32 + rq*8 + lg*4 + u.
+        if (c.i < c.q_len) {
+            TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)c.i * p.o_sn;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    typedef TO TO4 __attribute__((ext_vector_type(4)));
+                    TO4 w;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) w[u] = to_t(o[db][rq * 4 + u] * factor, (TO*)nullptr);
+                    *(TO4*)(orow + db * 32 + rq * 8 + lg * 4) = w;
+                }
+        }
+    }
+};
+
+template <typename TI, int D>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * Cfg<TI, D>::STAGE];
+    Prefill<TI, D>::run(p, smem);
+}
+
+template <typename TI, int D>
+static hipError_t launch_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    hipLaunchKernelGGL((prefill_kernel<TI, D>), dim3(grid_x, grid_y), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
+                          hipStream_t stream) {
+    if (elem == ELEM_F16) return head_dim == 64 ? launch_t<f16, 64>(p, grid_x, grid_y, stream)
+                                                : launch_t<f16, 128>(p, grid_x, grid_y, stream);
+    if (elem == ELEM_BF16) return head_dim == 64 ? launch_t<bf16, 64>(p, grid_x, grid_y, stream)
+                                                 : launch_t<bf16, 128>(p, grid_x, grid_y, stream);
+    return head_dim == 64 ? launch_t<fp8, 64>(p, grid_x, grid_y, stream)
+                          : launch_t<fp8, 128>(p, grid_x, grid_y, stream);
+}
+
+}  // namespace gqa

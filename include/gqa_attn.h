@@ -1,0 +1,165 @@
+/*
+ * gqa_attn.h -- C ABI of the fused ragged GQA attention library (gfx950).
+ *
+ * The operator is the one defined on the onnx-tensorrt "TensorRT Custom
+ * Operator Schemas" page:
+ *   - TRT_Attention: BMM1 -> mask -> normalization -> BMM2, with Q and KV
+ *     each in "padded_bhnd" [B,H,N,D] or "packed_nhd" [T,H,D] form
+ *     (tensor format notation; attributes query_form / kv_form /
+ *     causal_kind / TRT_normalization_op; inputs attn_mask, query_lengths,
+ *     kv_lengths; output Y with Q's shape, form and dtype);
+ *   - TRT_QuantizedAttention: the same plus a quantize-dequantize of the
+ *     normalized scores between normalization and BMM2
+ *     (normalization_quantize_to_type, normalization_quantize_scale), with
+ *     grouped-query heads (q_num_heads / kv_num_heads).
+ * The KV-cache data type option (FP16 or FP8) follows the TensorRT
+ * Edge-LLM "TensorRT Plugins Guide" page, AttentionPlugin section; an FP8
+ * cache carries one fp32 dequantization scale per tensor here.
+ *
+ * Conventions that the page leaves open (fixed here):
+ *   - Y = softmax(scale * Q K^T * k_descale + additive_mask) (V * v_descale)
+ *     with the grouped-query map  kv_head = q_head / (H_q / H_kv);
+ *   - scale is always explicit: pass 1.0f for TRT_Attention's "no implicit
+ *     scaling", 1/sqrt(D) for the ONNX default of the quantized op;
+ *   - causal upper_left allows key j <= i, lower_right allows
+ *     j <= i + kv_len_b - q_len_b (per-sequence valid lengths); both may be
+ *     combined with a mask (bool: AND; additive: added after scaling; an
+ *     additive -inf removes the key);
+ *   - a mask of rank <= 4 is right-aligned to [B, H_q, Nq, Nkv]; size-1
+ *     dimensions broadcast; (i, j) index the row / key within sequence b;
+ *   - a query row with no allowed key produces zeros;
+ *   - Q/DQ: x = P / qscale, round half to even, saturate (fp8 E4M3FN to
+ *     +-448, int8 to [-128,127]), P' = code * qscale; applied to the
+ *     normalized P, no renormalization;
+ *   - output rows that are not valid (padded rows i >= q_len_b, packed rows
+ *     beyond query_lengths[B]) are never written, and padding of Q/K/V is
+ *     never read.
+ *
+ * Ownership: the caller owns every buffer (all device pointers unless noted);
+ * the library never allocates, frees or synchronizes on the forward path
+ * and launches asynchronously on the caller's stream.
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of tensors. */
+typedef enum {
+    GQA_DT_F16 = 0,      /* IEEE binary16 */
+    GQA_DT_BF16 = 1,     /* bfloat16 */
+    GQA_DT_FP8_E4M3 = 2, /* OCP FP8 E4M3FN (max 448, no inf) */
+    GQA_DT_F32 = 3,      /* additive masks only */
+    GQA_DT_BOOL = 4      /* one byte, nonzero = may attend; masks only */
+} gqa_dtype_t;
+
+typedef enum { GQA_FORM_PADDED_BHND = 0, GQA_FORM_PACKED_NHD = 1 } gqa_form_t;
+typedef enum {
+    GQA_CAUSAL_NONE = 0,
+    GQA_CAUSAL_UPPER_LEFT = 1,
+    GQA_CAUSAL_LOWER_RIGHT = 2
+} gqa_causal_t;
+typedef enum { GQA_NORM_SOFTMAX = 0, GQA_NORM_NONE = 1 } gqa_norm_t;
+typedef enum { GQA_QDQ_OFF = 0, GQA_QDQ_FP8_E4M3 = 1, GQA_QDQ_INT8 = 2 } gqa_qdq_t;
+
+/* Status codes. Host-detectable errors are returned before any launch. */
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1, /* shapes, ranks, forms, missing lengths, heads ... */
+    GQA_ERR_UNSUPPORTED = 2, /* a valid combination this build has no kernel for */
+    GQA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    GQA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} gqa_status_t;
+
+/* A strided tensor view.  Strides are in elements; the last (head_size)
+ * dimension must have stride 1.  data == NULL marks an absent optional
+ * tensor (attn_mask). */
+typedef struct {
+    void* data;
+    int32_t dtype; /* gqa_dtype_t */
+    int32_t ndim;
+    int64_t shape[4];
+    int64_t stride[4];
+} gqa_tensor_t;
+
+/* Everything one forward call needs except the workspace and stream.
+ *
+ * q:   padded [B, H_q, N_q, D] or packed [T_q, H_q, D]; f16, bf16 or fp8.
+ * k,v: padded [B, H_kv, N_kv, D] or packed [T_kv, H_kv, D]; same dtype as
+ *      q, or fp8 with f16/bf16 q (an FP8 KV cache, dequantized with
+ *      k_descale / v_descale).
+ * attn_mask: optional, rank 1..4, bool or f16/bf16/f32 additive.
+ * query_lengths: device int32 [B+1], cumulative, starting at 0.  Required
+ *      when q is packed; optional when padded (then rows i >= q_len_b are
+ *      padding).
+ * kv_lengths: device int32.  KV packed: cumulative [B+1], required.  KV
+ *      padded: per-sequence lengths [B], optional (NULL = N_kv).
+ * batch: B.  Must equal q.shape[0] / k.shape[0] for padded forms; when both
+ *      forms are packed it is the only source of B on the host.
+ * out: Y in q's form and shape; dtype of q, except f16 when q is fp8.
+ *
+ * Device-side length preconditions (not checked on the host, which never
+ * reads device memory): lengths non-negative and monotone, query_lengths[0]
+ * = kv_lengths[0] = 0 when cumulative, query_lengths[B] <= T_q,
+ * kv_lengths[B] <= T_kv, q_len_b <= N_q and kv_len_b <= N_kv for padded
+ * forms, and the mask's query / key extents cover q_len_b / kv_len_b. */
+typedef struct {
+    gqa_tensor_t q, k, v;
+    gqa_tensor_t attn_mask;
+    gqa_tensor_t out;
+    const int32_t* query_lengths;
+    const int32_t* kv_lengths;
+    int32_t batch;
+    int32_t query_form;  /* gqa_form_t */
+    int32_t kv_form;     /* gqa_form_t */
+    int32_t causal_kind; /* gqa_causal_t */
+    int32_t norm;        /* gqa_norm_t */
+    int32_t qdq;         /* gqa_qdq_t */
+    float scale;         /* multiplies Q K^T */
+    float qscale;        /* normalization_quantize_scale; used iff qdq != OFF */
+    float k_descale;     /* 1.0f unless K is an fp8 cache */
+    float v_descale;     /* 1.0f unless V is an fp8 cache */
+    int32_t num_heads;    /* H_q */
+    int32_t kv_num_heads; /* H_kv; H_q % H_kv == 0 */
+} gqa_attn_args_t;
+
+/* Check every host-visible property of args; launches nothing, touches no
+ * device memory.  Returns a gqa_status_t. */
+int gqa_attn_validate(const gqa_attn_args_t* args);
+
+/* Bytes of device workspace gqa_attn_forward needs for args (0 when the
+ * selected kernels need none).  Returns a gqa_status_t; *bytes is written
+ * on success. */
+int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
+
+/* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
+ * stream).  workspace: device memory of at least gqa_attn_workspace_size
+ * bytes (may be NULL when that is 0), owned by the caller and not used by
+ * any other in-flight call.  Returns GQA_OK once the kernels are enqueued;
+ * a HIP launch error returns GQA_ERR_HIP (see gqa_attn_last_hip_error). */
+int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Human-readable text of a status code (static storage). */
+const char* gqa_attn_status_str(int status);
+
+/* Detail of the last failing call on this thread (static per-thread
+ * storage): which argument was rejected, or the HIP error string. */
+const char* gqa_attn_last_error(void);
+
+/* The hipError_t of the last GQA_ERR_HIP on this thread (0 if none). */
+int gqa_attn_last_hip_error(void);
+
+/* Library ABI version (bumped on any change of these declarations). */
+int gqa_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -1,0 +1,168 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/gqa_attn.h declares, and its host-only entry points
+(validate, workspace_size, status strings) behave as documented.  No call
+here touches device memory: descriptors carry fake, aligned pointers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gqa_attention_ragged_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+F16, BF16, FP8, F32, BOOL = 0, 1, 2, 3, 4
+PADDED, PACKED = 0, 1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gqa_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = capi.load()
+    names = declared_functions()
+    assert len(names) >= 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.gqa_attn_abi_version() == 1
+
+
+_addr = [0x100000]
+
+
+def fake(shape, dtype=F16, strides=None):
+    t = capi.GqaTensor()
+    _addr[0] += 0x1000000
+    t.data = _addr[0]
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, s = [], 1
+        for n in reversed(shape):
+            strides.insert(0, s)
+            s *= n
+    for d, (n, st) in enumerate(zip(shape, strides)):
+        t.shape[d] = n
+        t.stride[d] = st
+    return t
+
+
+def base_args(qf=PADDED, kf=PADDED, B=2, hq=8, hkv=2, nq=64, nkv=80, D=128, dt=F16, kvdt=None):
+    a = capi.GqaArgs()
+    kvdt = dt if kvdt is None else kvdt
+    a.q = fake([B, hq, nq, D] if qf == PADDED else [B * nq, hq, D], dt)
+    a.k = fake([B, hkv, nkv, D] if kf == PADDED else [B * nkv, hkv, D], kvdt)
+    a.v = fake([B, hkv, nkv, D] if kf == PADDED else [B * nkv, hkv, D], kvdt)
+    a.out = fake([B, hq, nq, D] if qf == PADDED else [B * nq, hq, D], F16 if dt == FP8 else dt)
+    a.attn_mask = capi.GqaTensor()
+    a.query_lengths = 0x7000000 if qf == PACKED else None
+    a.kv_lengths = 0x7100000 if kf == PACKED else None
+    a.batch = B
+    a.query_form, a.kv_form = qf, kf
+    a.scale, a.qscale, a.k_descale, a.v_descale = 0.125, 1.0, 1.0, 1.0
+    a.num_heads, a.kv_num_heads = hq, hkv
+    return a
+
+
+def st(a):
+    return capi.gqa_attn_validate(a)
+
+
+def test_valid_forms_pass():
+    for qf in (PADDED, PACKED):
+        for kf in (PADDED, PACKED):
+            for dt in (F16, BF16):
+                assert st(base_args(qf, kf, dt=dt)) == capi.GQA_OK, capi.last_error()
+
+
+def test_status_strings():
+    for s in range(5):
+        assert capi.status_str(s)
+    assert capi.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "num_heads", 7), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a, "kv_num_heads", 3), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a, "batch", 3), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a, "query_form", 5), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a, "causal_kind", 3), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a, "qdq", 7), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a.q, "data", None), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a.q, "ndim", 3), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: a.k.stride.__setitem__(3, 2), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a.v, "dtype", BF16), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a.out, "dtype", BF16), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: a.out.shape.__setitem__(2, 63), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: a.v.shape.__setitem__(2, 81), capi.GQA_ERR_INVALID_ARG),
+    (lambda a: setattr(a.q, "data", a.q.data + 2), capi.GQA_ERR_UNSUPPORTED),
+    (lambda a: a.q.stride.__setitem__(2, 130), capi.GQA_ERR_UNSUPPORTED),
+])
+def test_invalid_arguments(mutate, code):
+    a = base_args()
+    mutate(a)
+    assert st(a) == code, capi.last_error()
+    assert capi.last_error()
+
+
+def test_packed_requires_lengths():
+    a = base_args(PACKED, PADDED)
+    a.query_lengths = None
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    assert "query_lengths" in capi.last_error()
+    a = base_args(PADDED, PACKED)
+    a.kv_lengths = None
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    assert "kv_lengths" in capi.last_error()
+
+
+def test_head_size_and_dtype_support():
+    assert st(base_args(D=96)) == capi.GQA_ERR_UNSUPPORTED
+    assert st(base_args(D=64)) == capi.GQA_OK
+    a = base_args(dt=FP8)  # fp8 Q/K/V needs fp8 Q/DQ of the scores
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+    a.qdq, a.qscale = 1, 1 / 448
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a.qscale = 0.0
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    # fp8 KV cache with f16 Q: decode step only
+    assert st(base_args(kvdt=FP8)) == capi.GQA_ERR_UNSUPPORTED
+    assert st(base_args(nq=1, kvdt=FP8)) == capi.GQA_OK, capi.last_error()
+
+
+def test_mask_validation():
+    a = base_args()
+    a.attn_mask = fake([2, 1, 64, 80], BOOL)
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a.attn_mask = fake([64, 80], F32)
+    assert st(a) == capi.GQA_OK
+    a.attn_mask = fake([3, 1, 64, 80], BOOL)
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a.attn_mask = fake([2, 5, 64, 80], BOOL)
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a.attn_mask = fake([2, 1, 64, 79], F16)  # shorter than N_kv with no kv_lengths
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a.attn_mask = fake([2, 1, 64, 80], FP8)
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+
+
+def test_workspace_sizes():
+    # prefill needs none; the decode step (N_q = 1) needs split partials
+    assert capi.gqa_attn_workspace_size(base_args()) == 0
+    a = base_args(B=128, hq=32, hkv=8, nq=1, nkv=32768)
+    n = capi.gqa_attn_workspace_size(a)
+    assert n > 128 * 32 * 130 * 4
+    assert n < 1 << 30
+
+
+def test_empty_batch_is_valid():
+    a = base_args(B=0)
+    assert st(a) == capi.GQA_OK
+    a = base_args(PACKED, PACKED, B=2)
+    a.q.shape[0] = 0
+    a.out.shape[0] = 0
+    assert st(a) == capi.GQA_OK

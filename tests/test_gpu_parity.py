@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases compare every valid row element by element and check that no
+padding row of the output was written; full-size workload cases compare
+sampled rows the oracle computes one by one.  Inputs are seeded and
+synthetic (gqa_attention_ragged_amd.synth); padding is NaN-poisoned, so a
+kernel that reads it produces NaN in a valid row.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+from gqa_attention_ragged_amd import capi, synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _lens(rng, B, lo, hi):
+    return rng.integers(lo, hi + 1, size=B)
+
+
+def _case(seed, *, qf, kf, causal="none", mask=None, dtype=torch.float16, D=128, hq=8, hkv=2,
+          norm="softmax", qdq=None, B=3, qmax=150, kvmax=170, zero=False, n_q_pad=None,
+          kv_fp8=False, mask_heads=1):
+    rng = np.random.default_rng(seed)
+    ql = _lens(rng, B, 0 if zero else 1, qmax)
+    kl = _lens(rng, B, 0 if zero else 1, kvmax)
+    if causal == "lower_right" and not zero:
+        kl = np.maximum(kl, ql)
+    pass_ql = qf == "packed_nhd" or seed % 2 == 1
+    n_q = int(ql.max()) + 5 if n_q_pad is None else n_q_pad
+    if not pass_ql:
+        ql = np.full(B, n_q)
+        if causal == "lower_right":
+            kl = np.maximum(kl, ql)
+    return synth.generate(
+        seed=seed, q_lens=ql, kv_lens=kl, num_heads=hq, kv_num_heads=hkv, head_dim=D,
+        query_form=qf, kv_form=kf, dtype=dtype, n_q=n_q, n_kv=int(kl.max()) + 7, q_slack=3,
+        kv_slack=2, pass_query_lengths=pass_ql, mask_kind=mask, mask_heads=mask_heads,
+        mask_p=0.2, mask_value=-4.0 if seed % 3 else -float("inf"), mask_diag_true=True,
+        causal_kind=causal, norm=norm, qdq=qdq,
+        qscale=float(np.float32(1 / 448.0)) if qdq == "fp8" else 1 / 64.0,
+        kv_fp8_from=torch.float16 if kv_fp8 else None,
+        kv_dtype=torch.float8_e4m3fn if kv_fp8 else None,
+        dist="round_normal" if dtype == torch.float8_e4m3fn else "normal",
+        device=DEV, name=f"s{seed}-{qf[:3]}-{kf[:3]}-{causal}-{mask}-{dtype}-{D}-{hq}/{hkv}")
+
+
+FORMS = ["padded_bhnd", "packed_nhd"]
+
+
+def test_config1_full():
+    c = synth.make_config("1", device=DEV)
+    out = parity.run_gpu(c)
+    st = parity.compare(c, out)
+    assert st["rows"] == 2 * 4 * 128
+
+
+@pytest.mark.parametrize("qf,kf", list(itertools.product(FORMS, FORMS)))
+@pytest.mark.parametrize("causal", ["none", "upper_left", "lower_right"])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_forms_causal(qf, kf, causal, dtype):
+    seed = 100 + FORMS.index(qf) * 10 + FORMS.index(kf) * 5 + ["none", "upper_left",
+                                                              "lower_right"].index(causal)
+    c = _case(seed, qf=qf, kf=kf, causal=causal, dtype=dtype)
+    parity.compare(c, parity.run_gpu(c))
+
+
+@pytest.mark.parametrize("mask", ["bool", "f16", "bf16", "f32"])
+@pytest.mark.parametrize("causal", ["none", "lower_right"])
+@pytest.mark.parametrize("mask_heads", [1, 8])
+def test_masks(mask, causal, mask_heads):
+    seed = 200 + ["bool", "f16", "bf16", "f32"].index(mask) * 4 + (causal == "none") * 2 + (
+        mask_heads == 8)
+    c = _case(seed, qf="packed_nhd", kf="padded_bhnd", causal=causal, mask=mask,
+              mask_heads=mask_heads)
+    parity.compare(c, parity.run_gpu(c))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("heads", [(4, 4), (8, 4), (8, 2), (8, 1), (12, 4), (6, 2)])
+def test_head_groups_and_head_size(D, heads):
+    hq, hkv = heads
+    c = _case(300 + D + hq * 3 + hkv, qf="packed_nhd", kf="packed_nhd", causal="lower_right",
+              D=D, hq=hq, hkv=hkv, dtype=torch.bfloat16)
+    parity.compare(c, parity.run_gpu(c))
+
+
+def test_ragged_with_empty_sequences():
+    c = synth.generate(seed=401, q_lens=[0, 5, 0, 64, 1, 33], kv_lens=[3, 0, 0, 70, 1, 200],
+                       num_heads=8, kv_num_heads=2, head_dim=128, query_form="packed_nhd",
+                       kv_form="packed_nhd", causal_kind="lower_right", q_slack=4, kv_slack=4,
+                       device=DEV, name="empties")
+    out = parity.run_gpu(c)
+    parity.compare(c, out)
+
+
+@pytest.mark.parametrize("norm,qdq", [("none", None), ("none", "fp8"), ("none", "int8"),
+                                      ("softmax", "fp8"), ("softmax", "int8")])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_norm_and_qdq_16bit(norm, qdq, dtype):
+    seed = 500 + ["none", "softmax"].index(norm) * 10 + [None, "fp8", "int8"].index(qdq)
+    c = _case(seed, qf="padded_bhnd", kf="packed_nhd", causal="upper_left", mask="bool",
+              dtype=dtype, norm=norm, qdq=qdq, qmax=90, kvmax=120)
+    parity.compare(c, parity.run_gpu(c), amb_rel=1e-4)
+
+
+@pytest.mark.parametrize("causal,mask", [("upper_left", None), ("upper_left", "bool"),
+                                         ("none", None), ("lower_right", "f16")])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp8_quantized(causal, mask, D):
+    seed = 600 + D + ["upper_left", "none", "lower_right"].index(causal) * 3 + (mask is not None)
+    c = _case(seed, qf="padded_bhnd", kf="padded_bhnd", causal=causal, mask=mask,
+              dtype=torch.float8_e4m3fn, D=D, qdq="fp8", qmax=200, kvmax=200)
+    parity.compare(c, parity.run_gpu(c))
+
+
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_small(kv, D):
+    rng = np.random.default_rng(700 + D)
+    B = 5
+    kl = rng.integers(1, 3000, size=B)
+    kl[1] = 1
+    dtype = torch.bfloat16 if kv == "bf16" else torch.float16
+    c = synth.generate(seed=700 + D, q_lens=np.ones(B, int), kv_lens=kl, num_heads=8,
+                       kv_num_heads=2, head_dim=D, n_q=1, n_kv=int(kl.max()) + 9, dtype=dtype,
+                       pass_query_lengths=False,
+                       kv_fp8_from=torch.float16 if kv == "fp8" else None,
+                       kv_dtype=torch.float8_e4m3fn if kv == "fp8" else None, device=DEV,
+                       name=f"decode-{kv}-{D}")
+    parity.compare(c, parity.run_gpu(c))
+
+
+def test_decode_with_query_lengths_skips_rows():
+    c = synth.generate(seed=710, q_lens=[1, 0, 1], kv_lens=[40, 50, 0], num_heads=4,
+                       kv_num_heads=1, head_dim=128, n_q=1, n_kv=64, pass_query_lengths=True,
+                       device=DEV, name="decode-ql")
+    parity.compare(c, parity.run_gpu(c))
+
+
+def test_packed_equals_padded_bitwise_and_deterministic():
+    c = _case(801, qf="padded_bhnd", kf="padded_bhnd", causal="lower_right", mask="f16",
+              dtype=torch.bfloat16, n_q_pad=None)
+    a = parity.run_gpu(c)
+    a2 = parity.run_gpu(c)
+    assert torch.equal(a.view(torch.int16), a2.view(torch.int16))
+    ql = np.concatenate([[0], np.cumsum(c.q_lens)]).astype(np.int32)
+    kl = np.concatenate([[0], np.cumsum(c.kv_lens)]).astype(np.int32)
+    qp = torch.cat([c.q[b, :, :c.q_lens[b]].transpose(0, 1) for b in range(c.batch)]).contiguous()
+    kp = torch.cat([c.k[b, :, :c.kv_lens[b]].transpose(0, 1) for b in range(c.batch)]).contiguous()
+    vp = torch.cat([c.v[b, :, :c.kv_lens[b]].transpose(0, 1) for b in range(c.batch)]).contiguous()
+    kw = c.kwargs()
+    kw.update(query_form="packed_nhd", kv_form="packed_nhd",
+              query_lengths=torch.from_numpy(ql).to(DEV), kv_lengths=torch.from_numpy(kl).to(DEV))
+    b2 = capi.attn_forward(qp, kp, vp, c.mask, **kw)
+    torch.cuda.synchronize()
+    for b in range(c.batch):
+        x = a[b, :, :c.q_lens[b]].transpose(0, 1)
+        y = b2[ql[b]:ql[b + 1]]
+        assert torch.equal(x.contiguous().view(torch.int16), y.view(torch.int16)), b
+
+
+# ---------------------------------------------------------------- full sizes
+@pytest.mark.parametrize("cfg", ["2", "3", "4a", "4b", "5a", "5b"])
+def test_workload_sampled(cfg):
+    c = synth.make_config(cfg, device=DEV)
+    out = parity.run_gpu(c)
+    rows = parity.sample_rows(c, n_per_seq=6 if c.batch <= 16 else 1, seed=int(cfg[0]))
+    st = parity.compare(c, out, rows=rows)
+    assert st["rows"] > 0
+    # no NaN anywhere in the valid rows of the output (padding poisoned with NaN)
+    if c.query_form == "packed_nhd":
+        assert not torch.isnan(out[: int(np.sum(c.q_lens))].float()).any()
+    else:
+        assert not torch.isnan(out.float()).any()
