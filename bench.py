@@ -1,0 +1,308 @@
+"""Benchmark of the fused ragged GQA attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one call of the operator through the C ABI on one batch of
+seeded synthetic input already resident in HBM.  The default workload is
+the packed/packed ragged causal GQA prefill (B=16, lengths ~ U[64, 2048],
+H_q=32, H_kv=8, D=128, bf16, lower_right).  W untimed steps, then K steps
+bracketed by stream synchronisation and timed with HIP events recorded on
+the stream the kernels run on.  The JSON line reports
+
+  value     algorithmic TFLOP/s (prefill: 4*D*allowed pairs; the extra
+            statistics pass of the quantized op is not counted) or GB/s
+            (decode: valid K/V bytes + Q + Y);
+  roofline  that rate against the MI355X peak of the bounding unit;
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same
+            workload on this host's cores (a reported baseline only);
+  secondary the other workload shapes measured the same way (decode
+            GB/s, chunked context, quantized fp8), unless --no-secondary.
+
+--profile-pass runs one copy of known size plus one step, untimed, for the
+rocprofv3 counter runs that calibrate and measure HBM traffic.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # dense MFMA TFLOP/s
+HBM_PEAK = 8000.0  # GB/s
+WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "1")
+KERNEL_SOURCES = {
+    "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
+                "gqa_attention_ragged_amd/csrc/device_common.h"],
+    "decode": ["gqa_attention_ragged_amd/csrc/decode.hip",
+               "gqa_attention_ragged_amd/csrc/device_common.h"],
+}
+
+
+def kernel_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_of(case) -> dict:
+    """Algorithmic work of one step: FLOP (prefill kernel) or bytes (decode)."""
+    D = case.q.shape[-1]
+    ql = np.asarray(case.q_lens, dtype=np.int64)
+    kl = np.asarray(case.kv_lens, dtype=np.int64)
+    if case.query_form == "padded_bhnd" and case.q.shape[2] == 1 and case.mask is None:
+        kv_b = case.k.element_size()
+        q_b = case.q.element_size()
+        byts = int(np.sum(kl)) * case.kv_num_heads * D * 2 * kv_b + \
+            case.batch * case.num_heads * D * (q_b + 2)
+        return {"kind": "decode", "bytes": byts}
+    pairs = 0
+    for b in range(case.batch):
+        i = np.arange(ql[b])
+        if case.causal_kind == "none":
+            n = np.full(ql[b], kl[b])
+        else:
+            diag = 0 if case.causal_kind == "upper_left" else kl[b] - ql[b]
+            n = np.clip(i + diag + 1, 0, kl[b])
+        pairs += int(n.sum())
+    pairs *= case.num_heads
+    return {"kind": "prefill", "flop": 4 * D * pairs, "pairs": pairs}
+
+
+def dtype_name(case) -> str:
+    import torch
+    return {torch.bfloat16: "bf16", torch.float16: "f16", torch.float8_e4m3fn: "fp8"}[case.q.dtype]
+
+
+def make_step(case):
+    import torch
+    from gqa_attention_ragged_amd import capi, synth
+    out = synth.sentinel_like(case.q.shape, case.out_dtype, case.q.device)
+    args = capi.make_args(case.q, case.k, case.v, case.mask, out, **case.kwargs())
+    n = capi.gqa_attn_workspace_size(args)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=case.q.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = capi.load()
+    import ctypes
+    pargs = ctypes.byref(args)
+    ws_ptr, ws_n = ws.data_ptr(), ws.numel()
+
+    def step():
+        st = lib.gqa_attn_forward(pargs, ws_ptr, ws_n, stream)
+        if st != 0:
+            raise capi.GqaError(st, capi.last_error())
+
+    step.keep = (out, ws, args)  # keep buffers alive
+    return step
+
+
+def time_steps(step, steps: int, warmup: int) -> float:
+    """Average ms per step over `steps` timed launches (HIP events)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def measure(cfg: str, steps: int, warmup: int) -> dict:
+    import torch
+    from gqa_attention_ragged_amd import synth
+    case = synth.make_config(cfg, device="cuda")
+    torch.cuda.synchronize()
+    w = work_of(case)
+    ms = time_steps(make_step(case), steps, warmup)
+    dt = dtype_name(case)
+    r = {"workload": cfg, "description": synth.DESCRIPTIONS[cfg], "ms_per_step": round(ms, 4),
+         "dtype": dt}
+    if w["kind"] == "decode":
+        gbs = w["bytes"] / (ms * 1e-3) / 1e9
+        r.update(metric="KV GB/s", value=round(gbs, 1), unit="GB/s", bytes=w["bytes"],
+                 roofline_frac=round(gbs / HBM_PEAK, 4), bound="hbm", peak=HBM_PEAK)
+    else:
+        tf = w["flop"] / (ms * 1e-3) / 1e12
+        r.update(metric="attention TFLOP/s", value=round(tf, 1), unit="TFLOP/s", flop=w["flop"],
+                 roofline_frac=round(tf / PEAK[dt], 4), bound="mfma", peak=PEAK[dt])
+    r["_case"] = case
+    return r
+
+
+def traffic_for(cfg: str, kind: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_cfg{cfg}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha(kind):
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The CPU oracle on a bounded sample of rows of the same workload."""
+    import oracle
+    from tests import parity
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    w = work_of(case)
+    # pick whole rows, last rows of each sequence first (the longest), until
+    # the estimated work fills the time budget at ~1 GFLOP/s per core
+    budget = seconds * cores * 1.0e9
+    rows, work = [], 0
+    rng = np.random.default_rng(0)
+    per_b = []
+    for b in range(case.batch):
+        L = int(case.q_lens[b])
+        if L:
+            per_b.append((b, L))
+    D = case.q.shape[-1]
+    while work < budget and len(rows) < 200000:
+        b, L = per_b[int(rng.integers(0, len(per_b)))]
+        i = int(rng.integers(0, L))
+        h = int(rng.integers(0, case.num_heads))
+        rows.append((b, h, i))
+        kvl = int(case.kv_lens[b])
+        if case.causal_kind == "none":
+            n = kvl
+        else:
+            diag = 0 if case.causal_kind == "upper_left" else kvl - L
+            n = max(0, min(kvl, i + diag + 1))
+        work += 4 * D * max(n, 1)
+    rows = np.asarray(rows, dtype=np.int32)
+    # host copies of the sequences involved (outside the timed region)
+    done_work = 0
+    t_all = 0.0
+    for b in np.unique(rows[:, 0]):
+        sel = rows[:, 0] == b
+        sub = parity.subcase(case, [int(b)])
+        r = rows[sel].copy()
+        r[:, 0] = 0
+        t0 = time.perf_counter()
+        res = oracle.attention(sub.q, sub.k, sub.v, sub.mask, rows=r, **sub.kwargs())
+        t_all += time.perf_counter() - t0
+        if w["kind"] == "prefill":
+            done_work += int(res.nallowed.sum()) * 4 * D
+        else:
+            kvl = int(case.kv_lens[b])
+            done_work += int(sel.sum()) * kvl * D * 2 * case.k.element_size()
+    if w["kind"] == "prefill":
+        val = done_work / t_all / 1e12
+        unit = "TFLOP/s"
+        desc = f"{len(rows)} sampled query rows (all their allowed keys), {done_work:.3e} FLOP"
+    else:
+        val = done_work / t_all / 1e9
+        unit = "GB/s"
+        desc = f"{len(rows)} sampled (b, head) rows, {done_work:.3e} KV bytes"
+    return {"value": float(f"{val:.6g}"), "unit": unit, "cores": int(os.environ["OMP_NUM_THREADS"]),
+            "kind": "oracle", "sample": desc, "seconds": round(t_all, 2)}
+
+
+def profile_pass(cfg: str) -> None:
+    """One 256 MiB device copy (counter calibration) and one step."""
+    import torch
+    from gqa_attention_ragged_amd import synth
+    case = synth.make_config(cfg, device="cuda")
+    step = make_step(case)
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_pass": cfg, "copy_bytes": n}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="2", choices=WORKLOADS)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--profile-pass", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {a.gpus} requested); the "
+              "operator shards by KV-head group or by sequence with no exchange, but no "
+              "multi-GPU path is built", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    from gqa_attention_ragged_amd import capi
+    capi.load()  # fails loudly if the HIP library is missing
+    if a.profile_pass:
+        profile_pass(a.workload)
+        return 0
+
+    main_r = measure(a.workload, a.steps, a.warmup)
+    case = main_r.pop("_case")
+    kind = "decode" if main_r["bound"] == "hbm" else "prefill"
+    per_launch = main_r["bytes"] if kind == "decode" else main_r["flop"]
+    traffic = traffic_for(a.workload, kind)
+    ach = main_r["value"]
+    roof = {"bound": main_r["bound"], "achieved": ach, "peak": main_r["peak"],
+            "unit": main_r["unit"], "frac": round(ach / main_r["peak"], 4), "traffic": traffic,
+            "kernel": "gqa::prefill_kernel" if kind == "prefill" else "gqa::decode_split_kernel",
+            "per_launch": per_launch}
+    secondary = {}
+    if not a.no_secondary:
+        for cfg in WORKLOADS:
+            if cfg == a.workload or cfg == "1":
+                continue
+            r = measure(cfg, max(5, a.steps // 2), 2)
+            r.pop("_case")
+            secondary[cfg] = r
+            torch.cuda.empty_cache()
+    cpu = None
+    if not a.no_cpu:
+        cpu = cpu_baseline(case, a.cpu_seconds)
+    line = {
+        "metric": "attention TFLOP/s (prefill) + KV GB/s (decode), % of MI355X roofline",
+        "value": main_r["value"],
+        "unit": main_r["unit"],
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_r["dtype"],
+        "data": "synthetic (seeded; lengths, masks and values drawn as the workload specifies)",
+        "config": {"workload": main_r["description"], "global_batch": int(case.batch),
+                   "seq_len": int(max(case.q_lens)), "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

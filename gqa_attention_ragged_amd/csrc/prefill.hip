@@ -133,6 +133,9 @@ __device__ __forceinline__ MaskGroup load_mask_group(const AttnParams& p, const 
 
 // ------------------------------------------------------------------ kernel
 enum PassKind { PASS_STATS = 0, PASS_ONLINE = 1, PASS_FIXED = 2, PASS_NONE = 3 };
+// Kernel modes: online softmax; softmax with Q/DQ of P (two passes);
+// "none" normalization (with or without Q/DQ).
+enum Mode { MODE_SOFTMAX = 0, MODE_SOFTMAX_QDQ = 1, MODE_NONE = 2 };
 
 template <typename TI, int D>
 struct Prefill {
@@ -141,6 +144,13 @@ struct Prefill {
     // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
     typedef typename std::conditional<C::FP8, f16, TI>::type T16;
     typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
+
+    typedef typename Vec8<T16>::type V8;
+    // BMM1 B operand held in registers for the whole kernel: 8 x 16-bit
+    // values per k-step, or 32 E4M3FN codes per k-step.
+    typedef typename std::conditional<C::FP8, i32x8, V8>::type QOp;
+    typedef QOp QRegs[C::QSTEPS];
+    typedef f32x16 ORegs[D / 32];
 
     // Per-workgroup state shared by the passes.
     struct Ctx {
@@ -154,7 +164,7 @@ struct Prefill {
         int i;                // this lane's query row
     };
 
-    __device__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
+    __device__ __forceinline__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
                                      ChunkT (&rk)[C::KPT], ChunkT (&rv)[C::KPT]) {
         const int t = threadIdx.x;
         const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
@@ -171,7 +181,7 @@ struct Prefill {
         }
     }
 
-    __device__ static void store_tile(char* stage, bool with_v, const ChunkT (&rk)[C::KPT],
+    __device__ __forceinline__ static void store_tile(char* stage, bool with_v, const ChunkT (&rk)[C::KPT],
                                       const ChunkT (&rv)[C::KPT]) {
         const int t = threadIdx.x;
         const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
@@ -207,14 +217,13 @@ struct Prefill {
     }
 
     // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.
-    __device__ static void bmm1(const char* sK, const void* qreg, f32x16 (&s)[2]) {
+    __device__ __forceinline__ static void bmm1(const char* sK, const QRegs& qreg, f32x16 (&s)[2]) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             f32x16 acc = {};
             const char* row = sK + (kb * 32 + lr) * C::KROW;
-            if (C::FP8) {
-                const i32x8* q8 = (const i32x8*)qreg;
+            if constexpr (C::FP8) {
 #pragma unroll
                 for (int ks = 0; ks < C::QSTEPS; ++ks) {
                     const u32x4* src = (const u32x4*)(row + ks * 64 + lg * 32);
@@ -222,15 +231,13 @@ struct Prefill {
                     i32x8 a;
                     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
                     a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-                    acc = mfma32_fp8(a, q8[ks], acc);
+                    acc = mfma32_fp8(a, qreg[ks], acc);
                 }
             } else {
-                typedef typename Vec8<T16>::type V8;
-                const V8* q16 = (const V8*)qreg;
 #pragma unroll
                 for (int ks = 0; ks < C::QSTEPS; ++ks) {
                     V8 a = *(const V8*)(row + (ks * 16 + lg * 8) * 2);
-                    acc = mfma32(a, q16[ks], acc);
+                    acc = mfma32(a, qreg[ks], acc);
                 }
             }
             s[kb] = acc;
@@ -239,7 +246,7 @@ struct Prefill {
 
     // Scale the raw scores and apply the causal / length / mask predicate.
     // Disallowed entries become -inf (softmax) or are flagged via 0 (none).
-    __device__ static void predicate(const AttnParams& p, const Ctx& c, int tile, f32x16 (&s)[2],
+    __device__ __forceinline__ static void predicate(const AttnParams& p, const Ctx& c, int tile, f32x16 (&s)[2],
                                      float sc, float ac, bool none_norm) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
         const int j0 = tile * C::BN;
@@ -287,8 +294,7 @@ struct Prefill {
     }
 
     // 16-bit BMM2: O^T += V^T P^T over one 64-key tile.
-    __device__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], f32x16* o) {
-        typedef typename Vec8<T16>::type V8;
+    __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -305,8 +311,7 @@ struct Prefill {
 
     // "none" normalization keeps unbounded scores: split each into a 16-bit
     // high part and a 16-bit remainder so BMM2 keeps ~fp32 accuracy.
-    __device__ static void bmm2_16_split(const char* sV, const f32x16 (&pv)[2], f32x16* o) {
-        typedef typename Vec8<T16>::type V8;
+    __device__ __forceinline__ static void bmm2_16_split(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -328,7 +333,7 @@ struct Prefill {
     }
 
     // fp8 BMM2: P' codes (E4M3FN) against V^T codes, one 64-key k-step.
-    __device__ static void bmm2_fp8(const char* sV, const i32x8& codes, f32x16* o) {
+    __device__ __forceinline__ static void bmm2_fp8(const char* sV, const i32x8& codes, ORegs& o) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
@@ -343,7 +348,7 @@ struct Prefill {
 
     // Quantize x (= P / qscale) and return the dequantized code value
     // (without the qscale factor, which the epilogue applies).
-    __device__ static float qdq_value(float x, int kind) {
+    __device__ __forceinline__ static float qdq_value(float x, int kind) {
         if (kind == 1) {
             uint32_t code = f32_to_e4m3_pair(x, 0.f);
             return e4m3_to_f32<0>(code);
@@ -354,9 +359,9 @@ struct Prefill {
 
     // One sweep over the key tiles of this workgroup.
     template <int KIND>
-    __device__ static void sweep(const AttnParams& p, const Ctx& c, char* smem, const void* qreg,
-                                 float sc, float ac, float& m_run, float& l_run, float inv,
-                                 f32x16* o) {
+    __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c, char* smem,
+                                                 const QRegs& qreg, float sc, float ac,
+                                                 float& m_run, float& l_run, float inv, ORegs& o) {
         const bool with_v = KIND != PASS_STATS;
         ChunkT rk[C::KPT], rv[C::KPT];
         if (c.ntiles > 0) {
@@ -379,7 +384,7 @@ struct Prefill {
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) s[kb][r] = qdq_value(s[kb][r] * inv, p.qdq);
-                        if (C::FP8) {
+                        if constexpr (C::FP8) {
                             i32x8 codes;
 #pragma unroll
                             for (int w = 0; w < 8; ++w) {
@@ -427,7 +432,7 @@ struct Prefill {
                     } else {
                         // final max known: P = exp2(s - m) / l, x = P / qscale
                         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-                        if (C::FP8) {
+                        if constexpr (C::FP8) {
                             i32x8 codes;
 #pragma unroll
                             for (int w = 0; w < 8; ++w) {
@@ -457,7 +462,8 @@ struct Prefill {
         }
     }
 
-    __device__ static void run(const AttnParams& p, char* smem) {
+    template <int MODE>
+    __device__ __forceinline__ static void run(const AttnParams& p, char* smem) {
         __shared__ int s_map[2];
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int lr = lane & 31, lg = lane >> 5;
@@ -521,16 +527,14 @@ struct Prefill {
         }
 
         // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg)
-        typedef typename Vec8<T16>::type V8;
-        V8 q16[C::FP8 ? 1 : C::QSTEPS];
-        i32x8 q8[C::FP8 ? C::QSTEPS : 1];
+        QRegs qreg;
         {
             const bool ok = c.i < c.q_len;
             const char* qrow = (const char*)p.q.ptr +
                                (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.i * p.q.sn) * C::ES;
 #pragma unroll
             for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                if (C::FP8) {
+                if constexpr (C::FP8) {
                     u32x4 lo = {}, hi = {};
                     if (ok) {
                         const u32x4* src = (const u32x4*)(qrow + ks * 64 + lg * 32);
@@ -540,30 +544,29 @@ struct Prefill {
                     i32x8 a;
                     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
                     a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-                    q8[ks % (C::FP8 ? C::QSTEPS : 1)] = a;
+                    qreg[ks] = a;
                 } else {
                     V8 a = {};
                     if (ok) a = *(const V8*)(qrow + (ks * 16 + lg * 8) * 2);
-                    q16[ks % (C::FP8 ? 1 : C::QSTEPS)] = a;
+                    qreg[ks] = a;
                 }
             }
         }
-        const void* qreg = C::FP8 ? (const void*)q8 : (const void*)q16;
 
-        f32x16 o[D / 32];
+        ORegs o;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.f;
-        const bool none_norm = p.norm_none != 0;
+        const bool none_norm = MODE == MODE_NONE;
         const float sc = none_norm ? p.scale * p.k_descale : p.scale * p.k_descale * kLog2e;
         const float ac = none_norm ? 1.f : kLog2e;
         float factor = p.v_descale;
 
-        if (none_norm) {
+        if constexpr (MODE == MODE_NONE) {
             const float inv = p.qdq ? 1.f / p.qscale : 1.f;
             sweep<PASS_NONE>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
             if (p.qdq) factor *= p.qscale;
-        } else if (p.qdq) {
+        } else if constexpr (MODE == MODE_SOFTMAX_QDQ) {
             sweep<PASS_STATS>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
             const float l_tot = l_run + __shfl_xor(l_run, 32);
             const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
@@ -593,15 +596,34 @@ struct Prefill {
     }
 };
 
-template <typename TI, int D>
+template <typename TI, int D, int MODE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) char smem[2 * Cfg<TI, D>::STAGE];
-    Prefill<TI, D>::run(p, smem);
+    Prefill<TI, D>::template run<MODE>(p, smem);
 }
 
 template <typename TI, int D>
 static hipError_t launch_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
-    hipLaunchKernelGGL((prefill_kernel<TI, D>), dim3(grid_x, grid_y), dim3(256), 0, stream, p);
+    const int mode = p.norm_none ? MODE_NONE : (p.qdq ? MODE_SOFTMAX_QDQ : MODE_SOFTMAX);
+    if constexpr (std::is_same<TI, fp8>::value) {
+        // fp8 Q/K/V always carry fp8 Q/DQ of the scores (host-checked)
+        if (mode == MODE_NONE)
+            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_NONE>), dim3(grid_x, grid_y), dim3(256),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX_QDQ>), dim3(grid_x, grid_y),
+                               dim3(256), 0, stream, p);
+    } else {
+        if (mode == MODE_NONE)
+            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_NONE>), dim3(grid_x, grid_y), dim3(256),
+                               0, stream, p);
+        else if (mode == MODE_SOFTMAX_QDQ)
+            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX_QDQ>), dim3(grid_x, grid_y),
+                               dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX>), dim3(grid_x, grid_y),
+                               dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
