@@ -30,25 +30,62 @@
 
 namespace gqa {
 
+// Order this wave's LDS traffic: every LDS access issued before completes
+// before any issued after (the V tile is written and read by different lanes
+// of the same wave).  Waits on LDS only (lgkmcnt(0)), never on the global
+// loads in flight, and stops the compiler from moving memory operations
+// across it.
+__device__ __forceinline__ void lds_wave_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) lds_h4* lds_h4_ptr;
+typedef __attribute__((address_space(3))) u32x2* lds_u2_ptr;
+
+// LDS transpose reads (gfx950).  Within each group of 16 lanes, lane L
+// supplies an address; ds_read_b64_tr_b16 gives lane 4q+c the 16-bit element
+// c of lanes 4k+q (k = 0..3), ds_read_b64_tr_b8 gives lane 8q+c the byte c of
+// lanes 2k+q (k = 0..7).  With row-major V, pointing lane 4k+q (2k+q) at
+// (key_k, d0 + 4q (8q)) hands lane i the values of keys key_k at d = d0 + i:
+// a column of V, i.e. a row of V^T, as the MFMA A operand wants it.
+__device__ __forceinline__ u32x2 lds_tr16(const char* p) {
+    lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h4_ptr)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 lds_tr8(const char* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                         (__attribute__((address_space(3))) i32x2*)(p)));
+}
+
 template <typename TQ, typename TKV, int D>
 struct Decode {
     static constexpr bool KV8 = std::is_same<TKV, fp8>::value;
     static constexpr int KES = KV8 ? 1 : 2;       // K/V element bytes
     static constexpr int KT = 32;                 // keys per wave tile
-    static constexpr int VROW = KT * 2 + 16;      // LDS bytes per V^T row (16-bit)
-    static constexpr int WAVE_LDS = D * VROW;
-    static constexpr int CH = D / 8;              // 8-element chunks per row
-    static constexpr int KG = 64 / CH;            // key groups per wave for V loads
-    static constexpr int KPL = KT / KG;           // keys per lane for V loads
+    static constexpr int ROWB = D * KES;          // bytes per V row (global and LDS)
+    static constexpr int VCH = ROWB / 16;         // 16-byte chunks per V row
+    static constexpr int VRPI = 64 / VCH;         // V rows per wave load
+    static constexpr int VINS = KT / VRPI;        // V loads per lane per tile
+    static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;  // rows per 256-byte bank line
+    static constexpr int WAVE_LDS = KT * ROWB;
     static constexpr int MERGE_FLOATS = D * 16 + 32;
+    static constexpr int LDS_BYTES =
+        4 * WAVE_LDS > 4 * MERGE_FLOATS * 4 ? 4 * WAVE_LDS : 4 * MERGE_FLOATS * 4;
     typedef typename Vec8<TQ>::type V8;
     typedef typename std::conditional<KV8, u32x2, u32x4>::type ChunkT;
 
-    // position of key o (0..31) in a V^T row: lane group g of the BMM2
-    // A operand then holds the keys its S^T accumulators hold.
-    __device__ static int vpos(int o) { return ((o & 15) >> 2) * 8 + (o >> 4) * 4 + (o & 3); }
+    // XOR swizzle of the 16-byte chunks of V row `key` in LDS, chosen so the
+    // transpose reads of one instruction (16 keys x 32 bytes for 16-bit V,
+    // 32 keys x 16 bytes for fp8 V) spread evenly over the LDS banks.
+    __device__ __forceinline__ static int swz(int key) {
+        if constexpr (KV8) return (key / RPL) % VCH;
+        else return 2 * ((key / RPL) % (VCH / 2));
+    }
 
-    __device__ static V8 to8(ChunkT c) {
+    __device__ __forceinline__ static V8 to8(ChunkT c) {
         if constexpr (KV8) {
             return e4m3x8_to<TQ>(c);
         } else {
@@ -56,7 +93,7 @@ struct Decode {
         }
     }
 
-    __device__ static void run(const AttnParams& p, char* smem) {
+    __device__ __forceinline__ static void run(const AttnParams& p, char* smem) {
         const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int l16 = lane & 15, g = lane >> 4;
@@ -92,50 +129,52 @@ struct Decode {
         for (int db = 0; db < D / 16; ++db) o[db] = f32x4{};
         float m_run = -INFINITY, l_run = 0.f;
 
-        const int vch = lane % CH, vkg = lane / CH;
-        for (int j0 = k0 + wave * KT; j0 < k1; j0 += 4 * KT) {
-            // ---- issue loads: K operand (2 blocks x D/32 steps), V rows
-            ChunkT ka[2][D / 32];
+        // V loads: lane -> (row lane / VCH of each group of VRPI rows, chunk lane % VCH)
+        const int vrow = lane / VCH, vch = lane % VCH;
+        // Q must be resident before the key loop (see the prefill kernel).
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+
+        // Registers of one 32-key tile: K operand (2 blocks x D/32 steps) and
+        // V chunks.  Two sets: the next tile is in flight while the current
+        // one is computed.
+        struct Tile {
+            ChunkT k[2][D / 32];
+            u32x4 v[VINS];
+        };
+        // Rows [0, k1) of this sequence: keys past the split's end read as
+        // zero without touching memory (and are masked below).
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, rows_bytes(k1, p.k.sn, D, KES));
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, rows_bytes(k1, p.v.sn, D, KES));
+        auto load = [&](Tile& t, int j0) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int j = j0 + kb * 16 + l16;
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    ka[kb][ks] = ChunkT{};
-                    if (j < k1)
-                        ka[kb][ks] = *(const ChunkT*)(kbase + ((int64_t)j * p.k.sn + ks * 32 + g * 8) * KES);
-                }
+                for (int ks = 0; ks < D / 32; ++ks)
+                    buf_load(krs, (uint32_t)(((int64_t)j * p.k.sn + ks * 32 + g * 8) * KES),
+                             t.k[kb][ks]);
             }
-            ChunkT vr[KPL];
 #pragma unroll
-            for (int u = 0; u < KPL; ++u) {
-                const int j = j0 + vkg * KPL + u;
-                vr[u] = ChunkT{};
-                if (j < k1) vr[u] = *(const ChunkT*)(vbase + ((int64_t)j * p.v.sn + vch * 8) * KES);
+            for (int i = 0; i < VINS; ++i) {
+                const int j = j0 + i * VRPI + vrow;
+                buf_load(vrs, (uint32_t)((int64_t)j * p.v.sn * KES + vch * 16), t.v[i]);
             }
+        };
+        auto compute = [&](const Tile& t, int j0) {
             // ---- S^T = K Q^T
             f32x4 st[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) acc = mfma16(to8(ka[kb][ks]), qreg[ks], acc);
+                for (int ks = 0; ks < D / 32; ++ks) acc = mfma16(to8(t.k[kb][ks]), qreg[ks], acc);
                 st[kb] = acc;
             }
-            // ---- V^T into this wave's LDS (16-bit), runs of 4 keys
+            // ---- V tile, row-major, into this wave's LDS (swizzled chunks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = vch * 8 + e;
-#pragma unroll
-                for (int run = 0; run < KPL / 4; ++run) {
-                    V8 v0 = to8(vr[run * 4 + 0]), v1 = to8(vr[run * 4 + 1]);
-                    V8 v2 = to8(vr[run * 4 + 2]), v3 = to8(vr[run * 4 + 3]);
-                    typedef TQ T4 __attribute__((ext_vector_type(4)));
-                    T4 w;
-                    w[0] = v0[e]; w[1] = v1[e]; w[2] = v2[e]; w[3] = v3[e];
-                    const int key = vkg * KPL + run * 4;
-                    *(T4*)(sv + d * VROW + vpos(key) * 2) = w;
-                }
+            for (int i = 0; i < VINS; ++i) {
+                const int row = i * VRPI + vrow;
+                *(u32x4*)(sv + row * ROWB + ((vch ^ swz(row)) * 16)) = t.v[i];
             }
             // ---- predicate + online softmax (lane: head l16, keys kb*16 + g*4 + r)
             float mx = -INFINITY;
@@ -167,24 +206,62 @@ struct Decode {
             m_run = m_new;
 #pragma unroll
             for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // ---- O^T += V^T P^T
+            lds_wave_sync();
+            // ---- O^T += V^T P^T.  A operand lane (d = l16, group g) element
+            // e holds key (e/4)*16 + g*4 + e%4, the key pb[e] belongs to.
 #pragma unroll
             for (int db = 0; db < D / 16; ++db) {
-                V8 a = *(const V8*)(sv + (db * 16 + l16) * VROW + g * 16);
+                V8 a;
+                if constexpr (KV8) {
+                    const int key = ((l16 >> 1) >> 2) * 16 + g * 4 + ((l16 >> 1) & 3);
+                    const int d = db * 16 + 8 * (l16 & 1);
+                    const u32x2 w = lds_tr8(sv + key * ROWB + (((d >> 4) ^ swz(key)) * 16) + (d & 15));
+                    a = to8(w);
+                } else {
+                    const int d = db * 16 + 4 * (l16 & 3);
+                    u32x2 lo, hi;
+                    {
+                        const int key = g * 4 + (l16 >> 2);
+                        lo = lds_tr16(sv + key * ROWB + (((d >> 3) ^ swz(key)) * 16) + (d & 7) * 2);
+                    }
+                    {
+                        const int key = 16 + g * 4 + (l16 >> 2);
+                        hi = lds_tr16(sv + key * ROWB + (((d >> 3) ^ swz(key)) * 16) + (d & 7) * 2);
+                    }
+                    u32x4 w;
+                    w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
+                    a = __builtin_bit_cast(V8, w);
+                }
                 o[db] = mfma16(a, pb, o[db]);
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            lds_wave_sync();
+        };
+
+        // Software pipeline over this wave's tiles: the loads of the next tile
+        // are always issued before the current one is computed (past the
+        // split's end they fall outside the buffer range: zeros, no traffic).
+        const int stride = 4 * KT;
+        int j0 = k0 + wave * KT;
+        if (j0 < k1) {
+            Tile a, bt;
+            load(a, j0);
+            while (true) {
+                load(bt, j0 + stride);
+                compute(a, j0);
+                j0 += stride;
+                if (j0 >= k1) break;
+                load(a, j0 + stride);
+                compute(bt, j0);
+                j0 += stride;
+                if (j0 >= k1) break;
+            }
         }
 
-        // ---- merge the 4 waves through LDS
+        // ---- merge the 4 waves through LDS (reusing the V tiles' space)
         l_run += __shfl_xor(l_run, 16);
         l_run += __shfl_xor(l_run, 32);
-        float* mg = (float*)(smem + 4 * WAVE_LDS) + wave * MERGE_FLOATS;
+        __syncthreads();
+        float* mg = (float*)smem + wave * MERGE_FLOATS;
         if (g == 0) {
             mg[l16] = m_run;
             mg[16 + l16] = l_run;
@@ -194,7 +271,7 @@ struct Decode {
 #pragma unroll
             for (int r = 0; r < 4; ++r) mg[32 + (db * 16 + g * 4 + r) * 16 + l16] = o[db][r];
         __syncthreads();
-        const float* m0 = (const float*)(smem + 4 * WAVE_LDS);
+        const float* m0 = (const float*)smem;
         for (int idx = tid; idx < G * D; idx += 256) {
             const int hh = idx / D, d = idx % D;
             float M = -INFINITY;
@@ -222,7 +299,7 @@ struct Decode {
 template <typename TQ, typename TKV, int D>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnParams p) {
     typedef Decode<TQ, TKV, D> K;
-    __shared__ __attribute__((aligned(16))) char smem[4 * K::WAVE_LDS + 4 * K::MERGE_FLOATS * 4];
+    __shared__ __attribute__((aligned(16))) char smem[K::LDS_BYTES];
     K::run(p, smem);
 }
 

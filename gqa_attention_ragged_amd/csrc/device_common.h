@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -124,6 +125,26 @@ __device__ __forceinline__ typename Vec8<T>::type e4m3x8_to(u32x2 w) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- buffer loads
+// A raw buffer resource over [base, base + bytes): loads whose range falls
+// outside return zero and touch no memory, so predicated tile loads need no
+// branches (branch-free loads also let the compiler count outstanding loads
+// exactly instead of draining them all).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4& v) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2& v) {
+    v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+// Bytes from a sequence's first row to the end of its row n-1 (0 if n <= 0).
+__device__ __forceinline__ uint32_t rows_bytes(int n, int64_t row_stride, int d, int es) {
+    return n > 0 ? (uint32_t)(((int64_t)(n - 1) * row_stride + d) * es) : 0u;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 

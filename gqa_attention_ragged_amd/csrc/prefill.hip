@@ -49,7 +49,19 @@ struct Cfg {
     static constexpr int CHUNKS = D / 8;            // 8-element chunks per row
     static constexpr int KPT = D / 32;              // keys per loader thread
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
+    static constexpr int VGROUPS = BN * ES / 16;    // 16-byte groups per V^T row
 };
+
+// Byte offset of element position `pos` of V^T row d.  The 16-byte groups of
+// a row are XOR-swizzled with the row's 8-row block so that the transposing
+// writes (8 rows d = c*8 + e per instruction) spread over the LDS banks; the
+// 16-byte MFMA-operand reads stay contiguous and conflict-free.
+template <typename C>
+__device__ __forceinline__ int vt_addr(int d, int pos) {
+    const int byte = pos * C::ES;
+    const int grp = (byte >> 4) ^ ((d >> 3) & (C::VGROUPS - 1));
+    return d * C::VROW + grp * 16 + (byte & 15);
+}
 
 // Position of key o (0..63 within a tile) inside an LDS V^T row, chosen so
 // that the lane group g of a BMM2 A-operand read sees, in register order,
@@ -136,8 +148,11 @@ enum PassKind { PASS_STATS = 0, PASS_ONLINE = 1, PASS_FIXED = 2, PASS_NONE = 3 }
 // Kernel modes: online softmax; softmax with Q/DQ of P (two passes);
 // "none" normalization (with or without Q/DQ).
 enum Mode { MODE_SOFTMAX = 0, MODE_SOFTMAX_QDQ = 1, MODE_NONE = 2 };
+constexpr float kLazyRescale = 8.0f;  // log2 units
+// s_waitcnt immediate: vmcnt(0), expcnt / lgkmcnt not waited on.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <typename TI, int D>
+template <typename TI, int D, bool HAS_MASK>
 struct Prefill {
     typedef Cfg<TI, D> C;
     typedef typename Chunk<TI>::type ChunkT;
@@ -160,6 +175,7 @@ struct Prefill {
         int wave_kv_end;      // keys this wave can see (causal)
         const char* kbase;    // K rows of (b, kv head)
         const char* vbase;
+        __amdgpu_buffer_rsrc_t krs, vrs;  // the same rows, valid keys only
         const char* mrow;     // mask row of this lane's query row (or null)
         int i;                // this lane's query row
     };
@@ -171,13 +187,9 @@ struct Prefill {
 #pragma unroll
         for (int kk = 0; kk < C::KPT; ++kk) {
             const int j = tile * C::BN + kg * C::KPT + kk;
-            rk[kk] = ChunkT{};
-            rv[kk] = ChunkT{};
-            if (j < c.kv_len) {
-                rk[kk] = *(const ChunkT*)(c.kbase + ((int64_t)j * p.k.sn + ch * 8) * C::ES);
-                if (with_v)
-                    rv[kk] = *(const ChunkT*)(c.vbase + ((int64_t)j * p.v.sn + ch * 8) * C::ES);
-            }
+            // keys >= kv_len lie outside the buffer range: zero, not read
+            buf_load(c.krs, (uint32_t)(((int64_t)j * p.k.sn + ch * 8) * C::ES), rk[kk]);
+            if (with_v) buf_load(c.vrs, (uint32_t)(((int64_t)j * p.v.sn + ch * 8) * C::ES), rv[kk]);
         }
     }
 
@@ -195,7 +207,7 @@ struct Prefill {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int d = ch * 8 + e;
-            char* dst = sV + d * C::VROW + pos * C::ES;
+            char* dst = sV + vt_addr<C>(d, pos);
             if (C::FP8) {
                 uint32_t w = 0;
 #pragma unroll
@@ -246,30 +258,31 @@ struct Prefill {
 
     // Scale the raw scores and apply the causal / length / mask predicate.
     // Disallowed entries become -inf (softmax) or are flagged via 0 (none).
-    __device__ __forceinline__ static void predicate(const AttnParams& p, const Ctx& c, int tile, f32x16 (&s)[2],
-                                     float sc, float ac, bool none_norm) {
-        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+    // Whether every (row, key) of this tile is allowed, so the raw scores can
+    // be used as they are (softmax folds the scale into its exp2 argument).
+    __device__ __forceinline__ static bool tile_is_full(const AttnParams& p, const Ctx& c, int tile,
+                                                        float sc) {
+        const int j0 = tile * C::BN;
+        return !HAS_MASK && j0 + C::BN <= c.kv_len && c.wr0 + 32 <= c.q_len &&
+               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag) && sc > 0.f;
+    }
+
+    // Scale the raw scores and apply the causal / length / mask predicate.
+    // Disallowed entries become -inf (softmax) or 0 (none).
+    __device__ __forceinline__ static void predicate(const AttnParams& p, const Ctx& c, int tile,
+                                                     f32x16 (&s)[2], float sc, float ac,
+                                                     bool none_norm) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
         const int j0 = tile * C::BN;
         const bool row_ok = c.i < c.q_len;
-        const bool full_rows = c.wr0 + 32 <= c.q_len;
-        const bool need = p.mask_kind != MASK_NONE || j0 + C::BN > c.kv_len || !full_rows ||
-                          (p.causal && j0 + C::BN - 1 > c.wr0 + c.diag);
         const float off = none_norm ? 0.f : -INFINITY;
-        if (!need) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] *= sc;
-            return;
-        }
-        (void)lr;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
                 const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
                 MaskGroup mg;
-                if (p.mask_kind != MASK_NONE && row_ok) {
+                if (HAS_MASK && row_ok) {
                     mg = load_mask_group(p, c.mrow, jg, c.kv_len);
                 } else {
 #pragma unroll
@@ -281,9 +294,9 @@ struct Prefill {
                     const int r = rq * 4 + u;
                     bool a = row_ok && j < c.kv_len && (p.causal == 0 || j <= c.i + c.diag);
                     float v = s[kb][r] * sc;
-                    if (p.mask_kind == MASK_BOOL) {
+                    if (HAS_MASK && p.mask_kind == MASK_BOOL) {
                         a = a && mg.ok[u];
-                    } else if (p.mask_kind != MASK_NONE) {
+                    } else if (HAS_MASK) {
                         a = a && !(__builtin_isinf(mg.add[u]) && mg.add[u] < 0.f);
                         v += mg.add[u] * ac;
                     }
@@ -303,7 +316,7 @@ struct Prefill {
             for (int e = 0; e < 8; ++e) b[e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                V8 a = *(const V8*)(sV + (db * 32 + lr) * C::VROW + (ks * 16 + lg * 8) * 2);
+                V8 a = *(const V8*)(sV + vt_addr<C>(db * 32 + lr, ks * 16 + lg * 8));
                 o[db] = mfma32(a, b, o[db]);
             }
         }
@@ -325,7 +338,7 @@ struct Prefill {
             }
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                V8 a = *(const V8*)(sV + (db * 32 + lr) * C::VROW + (ks * 16 + lg * 8) * 2);
+                V8 a = *(const V8*)(sV + vt_addr<C>(db * 32 + lr, ks * 16 + lg * 8));
                 o[db] = mfma32(a, bh, o[db]);
                 o[db] = mfma32(a, bl, o[db]);
             }
@@ -337,8 +350,9 @@ struct Prefill {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const u32x4* src = (const u32x4*)(sV + (db * 32 + lr) * C::VROW + lg * 32);
-            u32x4 lo = src[0], hi = src[1];
+            const int d = db * 32 + lr;
+            u32x4 lo = *(const u32x4*)(sV + vt_addr<C>(d, lg * 32));
+            u32x4 hi = *(const u32x4*)(sV + vt_addr<C>(d, lg * 32 + 16));
             i32x8 a;
             a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
             a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
@@ -377,8 +391,8 @@ struct Prefill {
             if (c.wave_rows && j0 < c.wave_kv_end) {
                 f32x16 s[2];
                 bmm1(stage, qreg, s);
-                predicate(p, c, it, s, sc, ac, KIND == PASS_NONE);
                 if (KIND == PASS_NONE) {
+                    predicate(p, c, it, s, sc, ac, true);
                     if (p.qdq) {
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
@@ -401,46 +415,66 @@ struct Prefill {
                         bmm2_16_split(stage + C::KBYTES, s, o);
                     }
                 } else {
+                    // Softmax in the exp2 domain.  On a fully allowed tile the
+                    // raw dot products are kept and the score scale is folded
+                    // into the exp2 argument (fma); otherwise the predicate
+                    // scales them and marks disallowed keys with -inf.
+                    float eff = sc;
+                    if (!tile_is_full(p, c, it, sc)) {
+                        predicate(p, c, it, s, sc, ac, false);
+                        eff = 1.f;
+                    }
                     float mx = -INFINITY;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+                    mx *= eff;
                     if (KIND != PASS_FIXED) {
                         mx = fmaxf(mx, __shfl_xor(mx, 32));
-                        const float m_new = fmaxf(m_run, mx);
-                        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                        const float alpha = fast_exp2(m_run - m_use);
+                        // Lazy rescaling: the reference max only moves when a
+                        // row's max grows by more than 2^8, so exp2 values stay
+                        // <= 256 and the O / l rescale is skipped for the wave
+                        // on most tiles.  O / l is unchanged by the choice of
+                        // reference.
+                        const bool upd = mx > m_run + kLazyRescale;
+                        if (__any(upd)) {
+                            const float m_new = upd ? mx : m_run;
+                            const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+                            l_run *= alpha;
+                            if (KIND == PASS_ONLINE) {
+#pragma unroll
+                                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                            }
+                            m_run = m_new;
+                        }
+                        const float m_use = m_run == -INFINITY ? 0.f : m_run;
                         float ls = 0.f;
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
-                                const float e = fast_exp2(s[kb][r] - m_use);
+                                const float e = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
                                 s[kb][r] = e;
                                 ls += e;
                             }
-                        l_run = l_run * alpha + ls;
-                        m_run = m_new;
-                        if (KIND == PASS_ONLINE) {
-#pragma unroll
-                            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-                            bmm2_16(stage + C::KBYTES, s, o);
-                        }
+                        l_run += ls;
+                        if (KIND == PASS_ONLINE) bmm2_16(stage + C::KBYTES, s, o);
                     } else {
-                        // final max known: P = exp2(s - m) / l, x = P / qscale
+                        // reference max and sum known: P = exp2(s - m) / l,
+                        // x = P / qscale = exp2(s - m) * inv
                         const float m_use = m_run == -INFINITY ? 0.f : m_run;
                         if constexpr (C::FP8) {
                             i32x8 codes;
 #pragma unroll
                             for (int w = 0; w < 8; ++w) {
                                 const int kb = w >> 2, r0 = (w & 3) * 4;
-                                float x0 = fast_exp2(s[kb][r0] - m_use) * inv;
-                                float x1 = fast_exp2(s[kb][r0 + 1] - m_use) * inv;
-                                float x2 = fast_exp2(s[kb][r0 + 2] - m_use) * inv;
-                                float x3 = fast_exp2(s[kb][r0 + 3] - m_use) * inv;
+                                float x0 = fast_exp2(__builtin_fmaf(s[kb][r0], eff, -m_use)) * inv;
+                                float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 1], eff, -m_use)) * inv;
+                                float x2 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2], eff, -m_use)) * inv;
+                                float x3 = fast_exp2(__builtin_fmaf(s[kb][r0 + 3], eff, -m_use)) * inv;
                                 uint32_t lo = f32_to_e4m3_pair(x0, x1);
                                 uint32_t hi = f32_to_e4m3_pair(x2, x3);
                                 codes[w] = (int)(lo | (hi << 16));
@@ -451,7 +485,8 @@ struct Prefill {
                             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                                 for (int r = 0; r < 16; ++r)
-                                    s[kb][r] = qdq_value(fast_exp2(s[kb][r] - m_use) * inv, p.qdq);
+                                    s[kb][r] = qdq_value(
+                                        fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use)) * inv, p.qdq);
                             bmm2_16(stage + C::KBYTES, s, o);
                         }
                     }
@@ -468,7 +503,10 @@ struct Prefill {
         const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
         const int lr = lane & 31, lg = lane >> 5;
         const int R = p.rows_per_wg;
-        const int tile = blockIdx.x;
+        // Tiles are enumerated sequence by sequence, row tile by row tile; the
+        // workgroups take them in reverse so that, under causal masking, the
+        // heaviest (last) row tiles of each sequence are dispatched first.
+        const int tile = gridDim.x - 1 - blockIdx.x;
 
         // ---- ragged tile map: tile -> (b, row tile within b), on wave 0
         if (wave == 0) {
@@ -519,8 +557,10 @@ struct Prefill {
         if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
         c.kbase = (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * C::ES;
         c.vbase = (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * C::ES;
+        c.krs = make_rsrc(c.kbase, rows_bytes(c.kv_len, p.k.sn, D, C::ES));
+        c.vrs = make_rsrc(c.vbase, rows_bytes(c.kv_len, p.v.sn, D, C::ES));
         c.mrow = nullptr;
-        if (p.mask_kind != MASK_NONE) {
+        if (HAS_MASK) {
             const int mes = p.mask_kind == MASK_BOOL ? 1 : (p.mask_kind == MASK_F32 ? 4 : 2);
             c.mrow = (const char*)p.mask +
                      ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)c.i * p.m_si) * mes;
@@ -551,6 +591,10 @@ struct Prefill {
                     qreg[ks] = a;
                 }
             }
+            // Q must be resident before the key loop: otherwise the compiler
+            // cannot tell the Q loads from the K/V prefetch of the loop and
+            // waits for every outstanding load before the first MFMA.
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
 
         ORegs o;
@@ -596,33 +640,33 @@ struct Prefill {
     }
 };
 
-template <typename TI, int D, int MODE>
+template <typename TI, int D, int MODE, bool HAS_MASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) char smem[2 * Cfg<TI, D>::STAGE];
-    Prefill<TI, D>::template run<MODE>(p, smem);
+    Prefill<TI, D, HAS_MASK>::template run<MODE>(p, smem);
+}
+
+template <typename TI, int D, int MODE>
+static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    if (p.mask_kind != MASK_NONE)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, true>), dim3(grid_x, grid_y), dim3(256), 0,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, false>), dim3(grid_x, grid_y), dim3(256), 0,
+                           stream, p);
 }
 
 template <typename TI, int D>
 static hipError_t launch_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const int mode = p.norm_none ? MODE_NONE : (p.qdq ? MODE_SOFTMAX_QDQ : MODE_SOFTMAX);
-    if constexpr (std::is_same<TI, fp8>::value) {
+    if (mode == MODE_NONE) {
+        launch_m<TI, D, MODE_NONE>(p, grid_x, grid_y, stream);
+    } else if (mode == MODE_SOFTMAX_QDQ || std::is_same<TI, fp8>::value) {
         // fp8 Q/K/V always carry fp8 Q/DQ of the scores (host-checked)
-        if (mode == MODE_NONE)
-            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_NONE>), dim3(grid_x, grid_y), dim3(256),
-                               0, stream, p);
-        else
-            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX_QDQ>), dim3(grid_x, grid_y),
-                               dim3(256), 0, stream, p);
+        launch_m<TI, D, MODE_SOFTMAX_QDQ>(p, grid_x, grid_y, stream);
     } else {
-        if (mode == MODE_NONE)
-            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_NONE>), dim3(grid_x, grid_y), dim3(256),
-                               0, stream, p);
-        else if (mode == MODE_SOFTMAX_QDQ)
-            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX_QDQ>), dim3(grid_x, grid_y),
-                               dim3(256), 0, stream, p);
-        else
-            hipLaunchKernelGGL((prefill_kernel<TI, D, MODE_SOFTMAX>), dim3(grid_x, grid_y),
-                               dim3(256), 0, stream, p);
+        if constexpr (!std::is_same<TI, fp8>::value)
+            launch_m<TI, D, MODE_SOFTMAX>(p, grid_x, grid_y, stream);
     }
     return hipGetLastError();
 }
