@@ -42,35 +42,45 @@ struct Cfg {
     static constexpr int ES = FP8 ? 1 : 2;          // element bytes
     static constexpr int BN = 64;                   // keys per tile
     static constexpr int KROW = D * ES + 16;        // LDS bytes per K row (padded)
-    static constexpr int VROW = BN * ES + 16;       // LDS bytes per V^T row (padded)
+    static constexpr int VROW = D * ES;             // LDS bytes per V row (row-major, swizzled)
     static constexpr int KBYTES = BN * KROW;
-    static constexpr int VBYTES = D * VROW;
+    static constexpr int VBYTES = BN * VROW;
     static constexpr int STAGE = KBYTES + VBYTES;
     static constexpr int CHUNKS = D / 8;            // 8-element chunks per row
     static constexpr int KPT = D / 32;              // keys per loader thread
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
-    static constexpr int VGROUPS = BN * ES / 16;    // 16-byte groups per V^T row
+    static constexpr int VUNITS = VROW / 16;        // 16-byte units per V row
+    static constexpr int RPL = VROW >= 256 ? 1 : 256 / VROW;  // V rows per 256-byte bank line
 };
 
-// Byte offset of element position `pos` of V^T row d.  The 16-byte groups of
-// a row are XOR-swizzled with the row's 8-row block so that the transposing
-// writes (8 rows d = c*8 + e per instruction) spread over the LDS banks; the
-// 16-byte MFMA-operand reads stay contiguous and conflict-free.
+// V is staged row-major; the 16-byte units of row `key` are XOR-swizzled so
+// that the transpose reads of one instruction (8 keys x 64 bytes for 16-bit
+// V, 16 keys x 32 bytes for fp8 V) spread evenly over the LDS banks.
 template <typename C>
-__device__ __forceinline__ int vt_addr(int d, int pos) {
-    const int byte = pos * C::ES;
-    const int grp = (byte >> 4) ^ ((d >> 3) & (C::VGROUPS - 1));
-    return d * C::VROW + grp * 16 + (byte & 15);
+__device__ __forceinline__ int v_swz(int key) {
+    if constexpr (C::FP8) return 2 * ((key / C::RPL) % (C::VUNITS / 2));
+    else return 4 * ((key / C::RPL) % (C::VUNITS / 4));
+}
+// Byte offset of element d of V row `key`.
+template <typename C>
+__device__ __forceinline__ int v_addr(int key, int d) {
+    const int byte = d * C::ES;
+    return key * C::VROW + (((byte >> 4) ^ v_swz<C>(key)) << 4) + (byte & 15);
 }
 
-// Position of key o (0..63 within a tile) inside an LDS V^T row, chosen so
-// that the lane group g of a BMM2 A-operand read sees, in register order,
-// exactly the keys whose probabilities the same lane group holds in its
-// S^T accumulator (see the PV step).  A bit permutation of o.
-template <bool FP8>
-__device__ __forceinline__ int vpos(int o) {
-    if (FP8) return ((o & 7) >> 2) * 32 + (o >> 5) * 16 + ((o & 31) >> 3) * 4 + (o & 3);
-    return (o >> 4) * 16 + ((o & 7) >> 2) * 8 + ((o & 15) >> 3) * 4 + (o & 3);
+typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+// LDS transpose reads (gfx950): within each group of 16 lanes,
+// ds_read_b64_tr_b16 gives lane 4q+c the 16-bit element c of lanes 4k+q
+// (k = 0..3) and ds_read_b64_tr_b8 gives lane 8q+c the byte c of lanes 2k+q
+// (k = 0..7).  Pointing lane 4k+q (2k+q) at (key_k, d0 + 4q (8q)) of a
+// row-major V hands lane i the keys key_k at d = d0 + i: one row of V^T.
+__device__ __forceinline__ u32x2 tr16(const char* p) {
+    lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) lds_h4*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 tr8(const char* p) {
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)p));
 }
 
 template <typename TI>
@@ -203,61 +213,47 @@ struct Prefill {
         for (int kk = 0; kk < C::KPT; ++kk)
             *(ChunkT*)(sK + (kg * C::KPT + kk) * C::KROW + ch * 8 * C::ES) = rk[kk];
         if (!with_v) return;
-        const int pos = vpos<C::FP8>(kg * C::KPT);  // KPT consecutive keys -> contiguous
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = ch * 8 + e;
-            char* dst = sV + vt_addr<C>(d, pos);
-            if (C::FP8) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int kk = 0; kk < C::KPT; ++kk) w |= chunk_elem(rv[kk], e) << (8 * kk);
-                if (C::KPT == 4) *(uint32_t*)dst = w;
-                else if (C::KPT == 2) *(uint16_t*)dst = (uint16_t)w;
-                else *(uint8_t*)dst = (uint8_t)w;
-            } else {
-                if (C::KPT == 4) {
-                    u32x2 w;
-                    w[0] = chunk_elem(rv[0], e) | (chunk_elem(rv[1], e) << 16);
-                    w[1] = chunk_elem(rv[2 % C::KPT], e) | (chunk_elem(rv[3 % C::KPT], e) << 16);
-                    *(u32x2*)dst = w;
-                } else {
-                    *(uint32_t*)dst = chunk_elem(rv[0], e) | (chunk_elem(rv[1 % C::KPT], e) << 16);
-                }
-            }
-        }
+        for (int kk = 0; kk < C::KPT; ++kk)
+            *(ChunkT*)(sV + v_addr<C>(kg * C::KPT + kk, ch * 8)) = rv[kk];
     }
 
-    // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.
+    // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.  The
+    // two 32-key blocks accumulate in alternation so that consecutive MFMAs
+    // never wait on each other's result.
     __device__ __forceinline__ static void bmm1(const char* sK, const QRegs& qreg, f32x16 (&s)[2]) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const char* row0 = sK + lr * C::KROW;
+        const char* row1 = sK + (32 + lr) * C::KROW;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 acc = {};
-            const char* row = sK + (kb * 32 + lr) * C::KROW;
+        for (int ks = 0; ks < C::QSTEPS; ++ks) {
             if constexpr (C::FP8) {
-#pragma unroll
-                for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                    const u32x4* src = (const u32x4*)(row + ks * 64 + lg * 32);
-                    u32x4 lo = src[0], hi = src[1];
-                    i32x8 a;
-                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-                    acc = mfma32_fp8(a, qreg[ks], acc);
+                i32x8 a0, a1;
+                {
+                    const u32x4 lo = *(const u32x4*)(row0 + ks * 64 + lg * 32);
+                    const u32x4 hi = *(const u32x4*)(row0 + ks * 64 + lg * 32 + 16);
+                    a0[0] = lo[0]; a0[1] = lo[1]; a0[2] = lo[2]; a0[3] = lo[3];
+                    a0[4] = hi[0]; a0[5] = hi[1]; a0[6] = hi[2]; a0[7] = hi[3];
                 }
+                {
+                    const u32x4 lo = *(const u32x4*)(row1 + ks * 64 + lg * 32);
+                    const u32x4 hi = *(const u32x4*)(row1 + ks * 64 + lg * 32 + 16);
+                    a1[0] = lo[0]; a1[1] = lo[1]; a1[2] = lo[2]; a1[3] = lo[3];
+                    a1[4] = hi[0]; a1[5] = hi[1]; a1[6] = hi[2]; a1[7] = hi[3];
+                }
+                s[0] = mfma32_fp8(a0, qreg[ks], s[0]);
+                s[1] = mfma32_fp8(a1, qreg[ks], s[1]);
             } else {
-#pragma unroll
-                for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                    V8 a = *(const V8*)(row + (ks * 16 + lg * 8) * 2);
-                    acc = mfma32(a, qreg[ks], acc);
-                }
+                const V8 a0 = *(const V8*)(row0 + (ks * 16 + lg * 8) * 2);
+                const V8 a1 = *(const V8*)(row1 + (ks * 16 + lg * 8) * 2);
+                s[0] = mfma32(a0, qreg[ks], s[0]);
+                s[1] = mfma32(a1, qreg[ks], s[1]);
             }
-            s[kb] = acc;
         }
     }
 
-    // Scale the raw scores and apply the causal / length / mask predicate.
-    // Disallowed entries become -inf (softmax) or are flagged via 0 (none).
     // Whether every (row, key) of this tile is allowed, so the raw scores can
     // be used as they are (softmax folds the scale into its exp2 argument).
     __device__ __forceinline__ static bool tile_is_full(const AttnParams& p, const Ctx& c, int tile,
@@ -306,6 +302,21 @@ struct Prefill {
         }
     }
 
+    // BMM2 A operand for k-step ks (16 keys) and d-block db (32 values of d):
+    // lane (d = db*32 + lane%32, g = lane/32) gets keys
+    // ks*16 + (e/4)*8 + g*4 + e%4 for e = 0..7 -- the keys whose
+    // probabilities the same lane holds in its S^T accumulator.
+    __device__ __forceinline__ static V8 v_operand(const char* sV, int ks, int db) {
+        const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 5, dh = (lane >> 4) & 1;
+        const int d = db * 32 + dh * 16 + 4 * (l16 & 3);
+        const int key = ks * 16 + g * 4 + (l16 >> 2);
+        const u32x2 lo = tr16(sV + v_addr<C>(key, d));
+        const u32x2 hi = tr16(sV + v_addr<C>(key + 8, d));
+        u32x4 w;
+        w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
+        return __builtin_bit_cast(V8, w);
+    }
+
     // 16-bit BMM2: O^T += V^T P^T over one 64-key tile.
     __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
@@ -316,7 +327,7 @@ struct Prefill {
             for (int e = 0; e < 8; ++e) b[e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                V8 a = *(const V8*)(sV + vt_addr<C>(db * 32 + lr, ks * 16 + lg * 8));
+                const V8 a = v_operand(sV, ks, db);
                 o[db] = mfma32(a, b, o[db]);
             }
         }
@@ -338,7 +349,7 @@ struct Prefill {
             }
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                V8 a = *(const V8*)(sV + vt_addr<C>(db * 32 + lr, ks * 16 + lg * 8));
+                const V8 a = v_operand(sV, ks, db);
                 o[db] = mfma32(a, bh, o[db]);
                 o[db] = mfma32(a, bl, o[db]);
             }
@@ -350,12 +361,17 @@ struct Prefill {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const int d = db * 32 + lr;
-            u32x4 lo = *(const u32x4*)(sV + vt_addr<C>(d, lg * 32));
-            u32x4 hi = *(const u32x4*)(sV + vt_addr<C>(d, lg * 32 + 16));
+            // four 8-key transpose reads; read t holds keys key(t, g, k)
+            const int l16 = lane & 15, dh = (lane >> 4) & 1, k = l16 >> 1;
+            const int d = db * 32 + dh * 16 + 8 * (l16 & 1);
             i32x8 a;
-            a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-            a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int key = (t >> 1) * 32 + ((t & 1) * 2 + (k >> 2)) * 8 + lg * 4 + (k & 3);
+                const u32x2 w = tr8(sV + v_addr<C>(key, d));
+                a[2 * t] = (int)w[0];
+                a[2 * t + 1] = (int)w[1];
+            }
             o[db] = mfma32_fp8(a, codes, o[db]);
         }
     }
