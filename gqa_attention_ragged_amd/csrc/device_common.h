@@ -39,6 +39,7 @@ struct AttnParams {
     int64_t m_sb, m_sh, m_si, m_sj;  // 0 on broadcast dimensions
     int32_t mask_kind;
     int32_t mask_vec;                 // 1 if 4-key groups of the mask are aligned & contiguous
+    int32_t mask_lds;                 // 1 if mask tiles are staged through LDS (see prefill)
     const int32_t* ql;                // cumulative query lengths or null
     const int32_t* kl;                // cumulative (packed KV) / per-batch (padded) / null
     int32_t q_packed, kv_packed;

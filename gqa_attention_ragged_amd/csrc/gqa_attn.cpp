@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -267,6 +268,19 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     const int R = 32 * (4 / hw);
     p.heads_per_wg = hw;
     p.rows_per_wg = R;
+    // Mask tiles shared by a workgroup's heads are staged through LDS when the
+    // mask broadcasts over heads, is 1 or 2 bytes wide with contiguous keys
+    // and 16-byte aligned rows whose key extent is a whole number of 16-byte
+    // chunks (tiles are loaded in 16-byte chunks), and the workgroup covers
+    // 32 rows.
+    p.mask_lds = 0;
+    if (m.data && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
+        (p.mask_kind == gqa::MASK_BOOL || p.mask_kind == gqa::MASK_F16 ||
+         p.mask_kind == gqa::MASK_BF16)) {
+        const int64_t es = p.mask_kind == gqa::MASK_BOOL ? 1 : 2;
+        p.mask_lds = (uintptr_t)m.data % 16 == 0 && (p.m_si * es) % 16 == 0 &&
+                     (p.m_sb * es) % 16 == 0 && (m.shape[m.ndim - 1] * es) % 16 == 0;
+    }
     int64_t gx = qf == GQA_FORM_PADDED_BHND ? B * ((Nq + R - 1) / R) : (Tq + R - 1) / R + B;
     if (gx > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many query tiles");
     plan->grid_x = (int)gx;
@@ -274,6 +288,27 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     if (plan->grid_y > 65535) return fail(GQA_ERR_UNSUPPORTED, "too many heads");
     plan->kernel = K_PREFILL;
     plan->workspace = 0;
+    p.n_splits = 1;
+    p.split_keys = 0;
+    // Split-KV for prefill: with too few query tiles to fill the GPU and long
+    // key ranges (chunked context), the keys of each tile are divided among
+    // several workgroups whose fp32 partials a combine kernel merges.  Only
+    // for online softmax (Q/DQ needs the full row before quantizing).
+    const int64_t wgs = (int64_t)plan->grid_x * plan->grid_y;
+    const int64_t kv_tiles = (kv_max + 63) / 64;
+    if (a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF && qdt != GQA_DT_FP8_E4M3 &&
+        wgs < 1536 && kv_tiles >= 8) {
+        int64_t S = (3072 + wgs - 1) / wgs;
+        S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));
+        if (S > 1) {
+            const int64_t per_tiles = (kv_tiles + S - 1) / S;
+            S = (kv_tiles + per_tiles - 1) / per_tiles;
+            const int64_t rows = qf == GQA_FORM_PACKED_NHD ? Tq : B * Nq;
+            p.n_splits = (int)S;
+            p.split_keys = (int)(per_tiles * 64);
+            plan->workspace = (size_t)rows * Hq * S * (D + 2) * sizeof(float) + 256;
+        }
+    }
     return GQA_OK;
 }
 
@@ -310,6 +345,16 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
         plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
         e = gqa::launch_decode(plan.p, plan.q_elem, plan.kv_elem, plan.head_dim, s);
     } else {
+        if (plan.p.n_splits > 1) {
+            if (!workspace || workspace_bytes < plan.workspace)
+                return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed", plan.workspace);
+            uintptr_t w = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+            const int64_t rows = plan.p.q_packed ? args->q.shape[0]
+                                                 : (int64_t)plan.p.batch * plan.p.n_q;
+            const int64_t slots = rows * plan.p.hq * plan.p.n_splits;
+            plan.p.part_o = (float*)w;
+            plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
+        }
         e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
     }
     if (e != hipSuccess) {

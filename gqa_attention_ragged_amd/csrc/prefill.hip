@@ -51,6 +51,10 @@ struct Cfg {
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
     static constexpr int VUNITS = VROW / 16;        // 16-byte units per V row
     static constexpr int RPL = VROW >= 256 ? 1 : 256 / VROW;  // V rows per 256-byte bank line
+    // Staged mask tile: 32 query rows x BN keys of a 1- or 2-byte mask
+    // (row stride padded by 16 bytes against bank conflicts).
+    static constexpr int MROW = BN * 2 + 16;
+    static constexpr int MBYTES = 32 * MROW;
 };
 
 // V is staged row-major; the 16-byte units of row `key` are XOR-swizzled so
@@ -153,6 +157,39 @@ __device__ __forceinline__ MaskGroup load_mask_group(const AttnParams& p, const 
     return m;
 }
 
+// ------------------------------------------------------------------ tile map
+// Row tile `tile` of the ragged batch -> (b, row tile within b), with the
+// tiles enumerated sequence by sequence (ceil(q_len_b / R) tiles each).
+// Wave 0 scans the per-sequence tile counts 64 sequences at a time; the
+// result lands in s_map[0..1] (b = -1 past the last tile).  Block-wide
+// barrier included.
+__device__ __forceinline__ void map_tile(const AttnParams& p, int tile, int R, int* s_map) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) {
+        if (lane == 0) s_map[0] = -1;
+        int acc = 0;
+        for (int base = 0; base < p.batch; base += 64) {
+            const int b = base + lane;
+            int n = 0;
+            if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
+            int incl = n;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int excl = incl - n;
+            if (n > 0 && tile >= acc + excl && tile < acc + incl) {
+                s_map[0] = b;
+                s_map[1] = tile - acc - excl;
+            }
+            acc += __shfl(incl, 63);
+            if (acc > tile) break;
+        }
+    }
+    __syncthreads();
+}
+
 // ------------------------------------------------------------------ kernel
 enum PassKind { PASS_STATS = 0, PASS_ONLINE = 1, PASS_FIXED = 2, PASS_NONE = 3 };
 // Kernel modes: online softmax; softmax with Q/DQ of P (two passes);
@@ -171,6 +208,8 @@ struct Prefill {
     typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
 
     typedef typename Vec8<T16>::type V8;
+    // Bytes per pipeline stage: K tile, V tile and (mask kernels) a mask tile.
+    static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? C::MBYTES : 0);
     // BMM1 B operand held in registers for the whole kernel: 8 x 16-bit
     // values per k-step, or 32 E4M3FN codes per k-step.
     typedef typename std::conditional<C::FP8, i32x8, V8>::type QOp;
@@ -179,27 +218,57 @@ struct Prefill {
 
     // Per-workgroup state shared by the passes.
     struct Ctx {
-        int b, q_len, kv_len, diag, ntiles;
+        int b, q_len, kv_len, diag;
+        int t0, t1;           // key tiles [t0, t1) of this workgroup
+        bool causal;
         int wr0;              // first row of this wave
         bool wave_rows;       // wave has at least one valid row
         int wave_kv_end;      // keys this wave can see (causal)
         const char* kbase;    // K rows of (b, kv head)
         const char* vbase;
-        __amdgpu_buffer_rsrc_t krs, vrs;  // the same rows, valid keys only
+        uint32_t kbytes, vbytes;        // bytes from row 0 to the end of the last valid key
+        uint32_t ktile, vtile;          // bytes per tile of BN keys
+        uint32_t koff[C::KPT], voff[C::KPT];  // this thread's load offsets inside a tile
         const char* mrow;     // mask row of this lane's query row (or null)
+        const char* mtile;    // staged mask: the workgroup's first mask row
+        uint32_t mvalid;      // staged mask: bytes up to the last valid (row, key)
+        uint32_t moff;        // staged mask: this thread's load offset in a tile
+        int mrow_l, mchunk;   // staged mask: this thread's (row, 16-byte chunk); row < 0: idle
         int i;                // this lane's query row
     };
 
+    // A buffer window starting at tile `tile`: the wave-uniform base moves
+    // with the tile (scalar arithmetic only) and the range ends with the last
+    // valid key, so keys >= kv_len read as zero and touch no memory.
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t window(const char* base,
+                                                                    uint32_t valid,
+                                                                    uint32_t stride, int tile) {
+        const uint32_t off = (uint32_t)tile * stride;
+        return make_rsrc(base + off, valid > off ? valid - off : 0u);
+    }
+
+    __device__ __forceinline__ static void load_mask(const AttnParams& p, const Ctx& c, int tile,
+                                                     u32x4& rm) {
+        const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
+        const uint32_t off = (uint32_t)tile * (uint32_t)(C::BN * es);
+        const __amdgpu_buffer_rsrc_t mr =
+            make_rsrc(c.mtile + off, c.mvalid > off ? c.mvalid - off : 0u);
+        buf_load(mr, c.moff, rm);
+    }
+    __device__ __forceinline__ static void store_mask(char* stage, const Ctx& c, const u32x4& rm) {
+        if (c.mrow_l >= 0) *(u32x4*)(stage + C::STAGE + c.mrow_l * C::MROW + c.mchunk * 16) = rm;
+    }
+
     __device__ __forceinline__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
                                      ChunkT (&rk)[C::KPT], ChunkT (&rv)[C::KPT]) {
-        const int t = threadIdx.x;
-        const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
+        (void)p;
+        const __amdgpu_buffer_rsrc_t kr = window(c.kbase, c.kbytes, c.ktile, tile);
 #pragma unroll
-        for (int kk = 0; kk < C::KPT; ++kk) {
-            const int j = tile * C::BN + kg * C::KPT + kk;
-            // keys >= kv_len lie outside the buffer range: zero, not read
-            buf_load(c.krs, (uint32_t)(((int64_t)j * p.k.sn + ch * 8) * C::ES), rk[kk]);
-            if (with_v) buf_load(c.vrs, (uint32_t)(((int64_t)j * p.v.sn + ch * 8) * C::ES), rv[kk]);
+        for (int kk = 0; kk < C::KPT; ++kk) buf_load(kr, c.koff[kk], rk[kk]);
+        if (with_v) {
+            const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
+#pragma unroll
+            for (int kk = 0; kk < C::KPT; ++kk) buf_load(vr, c.voff[kk], rv[kk]);
         }
     }
 
@@ -263,11 +332,28 @@ struct Prefill {
                !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag) && sc > 0.f;
     }
 
+    // Mask-free kernels: mark the keys a row may not see with -inf and keep
+    // the other raw scores (the scale is applied inside the exp2 argument).
+    // Key j of this lane's row is allowed iff j < lim, one compare per score.
+    __device__ __forceinline__ static void predicate_raw(const Ctx& c, int tile, f32x16 (&s)[2]) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        int lim = c.i < c.q_len ? c.kv_len : 0;
+        if (c.causal) lim = min(lim, c.i + c.diag + 1);
+        const int rel = lim - (tile * C::BN + lg * 4);  // key offset limit for this lane
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                s[kb][r] = off < rel ? s[kb][r] : -INFINITY;
+            }
+    }
+
     // Scale the raw scores and apply the causal / length / mask predicate.
     // Disallowed entries become -inf (softmax) or 0 (none).
     __device__ __forceinline__ static void predicate(const AttnParams& p, const Ctx& c, int tile,
                                                      f32x16 (&s)[2], float sc, float ac,
-                                                     bool none_norm) {
+                                                     bool none_norm, const char* stage) {
         const int lane = threadIdx.x & 63, lg = lane >> 5;
         const int j0 = tile * C::BN;
         const bool row_ok = c.i < c.q_len;
@@ -278,7 +364,26 @@ struct Prefill {
             for (int rq = 0; rq < 4; ++rq) {
                 const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
                 MaskGroup mg;
-                if (HAS_MASK && row_ok) {
+                if (HAS_MASK && p.mask_lds) {
+                    // staged tile: row = this lane's row within the 32-row tile
+                    const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+                    const int ko = kb * 32 + rq * 8 + lg * 4;
+                    if (p.mask_kind == MASK_BOOL) {
+                        const uint32_t w = *(const uint32_t*)(src + ko);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) { mg.ok[u] = (w >> (8 * u)) & 0xff; mg.add[u] = 0.f; }
+                    } else {
+                        const u32x2 w = *(const u32x2*)(src + ko * 2);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const uint32_t h16 = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
+                            mg.add[u] = p.mask_kind == MASK_F16
+                                            ? (float)__builtin_bit_cast(f16, (uint16_t)h16)
+                                            : __builtin_bit_cast(float, h16 << 16);
+                            mg.ok[u] = true;
+                        }
+                    }
+                } else if (HAS_MASK && row_ok) {
                     mg = load_mask_group(p, c.mrow, jg, c.kv_len);
                 } else {
 #pragma unroll
@@ -394,21 +499,28 @@ struct Prefill {
                                                  float& m_run, float& l_run, float inv, ORegs& o) {
         const bool with_v = KIND != PASS_STATS;
         ChunkT rk[C::KPT], rv[C::KPT];
-        if (c.ntiles > 0) {
-            load_tile(p, c, 0, with_v, rk, rv);
+        u32x4 rm = {};
+        const bool mlds = HAS_MASK && p.mask_lds;
+        if (c.t0 < c.t1) {
+            load_tile(p, c, c.t0, with_v, rk, rv);
+            if (mlds) load_mask(p, c, c.t0, rm);
             store_tile(smem, with_v, rk, rv);
+            if (mlds) store_mask(smem, c, rm);
         }
         __syncthreads();
-        for (int it = 0; it < c.ntiles; ++it) {
-            const bool more = it + 1 < c.ntiles;
+        // Loop body for tile `it` computed from `stage` while tile it+1 is
+        // staged into `nstage`; unrolled by two below so that both stage
+        // addresses are compile-time LDS offsets.
+        auto body = [&](int it, char* stage, char* nstage) {
+            const bool more = it + 1 < c.t1;
             if (more) load_tile(p, c, it + 1, with_v, rk, rv);
-            char* stage = smem + (it & 1) * C::STAGE;
+            if (mlds && more) load_mask(p, c, it + 1, rm);
             const int j0 = it * C::BN;
             if (c.wave_rows && j0 < c.wave_kv_end) {
                 f32x16 s[2];
                 bmm1(stage, qreg, s);
                 if (KIND == PASS_NONE) {
-                    predicate(p, c, it, s, sc, ac, true);
+                    predicate(p, c, it, s, sc, ac, true, stage);
                     if (p.qdq) {
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
@@ -437,8 +549,12 @@ struct Prefill {
                     // scales them and marks disallowed keys with -inf.
                     float eff = sc;
                     if (!tile_is_full(p, c, it, sc)) {
-                        predicate(p, c, it, s, sc, ac, false);
-                        eff = 1.f;
+                        if (!HAS_MASK && sc > 0.f) {
+                            predicate_raw(c, it, s);
+                        } else {
+                            predicate(p, c, it, s, sc, ac, false, stage);
+                            eff = 1.f;
+                        }
                     }
                     float mx = -INFINITY;
 #pragma unroll
@@ -508,9 +624,16 @@ struct Prefill {
                     }
                 }
             }
-            if (more) store_tile(smem + ((it + 1) & 1) * C::STAGE, with_v, rk, rv);
+            if (more) store_tile(nstage, with_v, rk, rv);
+            if (mlds && more) store_mask(nstage, c, rm);
             __syncthreads();
+        };
+        int it = c.t0;
+        for (; it + 1 < c.t1; it += 2) {
+            body(it, smem, smem + SSTAGE);
+            body(it + 1, smem + SSTAGE, smem);
         }
+        if (it < c.t1) body(it, smem, smem + SSTAGE);
     }
 
     template <int MODE>
@@ -524,30 +647,7 @@ struct Prefill {
         // heaviest (last) row tiles of each sequence are dispatched first.
         const int tile = gridDim.x - 1 - blockIdx.x;
 
-        // ---- ragged tile map: tile -> (b, row tile within b), on wave 0
-        if (wave == 0) {
-            if (lane == 0) s_map[0] = -1;
-            int acc = 0;
-            for (int base = 0; base < p.batch; base += 64) {
-                const int b = base + lane;
-                int n = 0;
-                if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
-                int incl = n;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    int y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
-                }
-                const int excl = incl - n;
-                if (n > 0 && tile >= acc + excl && tile < acc + incl) {
-                    s_map[0] = b;
-                    s_map[1] = tile - acc - excl;
-                }
-                acc += __shfl(incl, 63);
-                if (acc > tile) break;
-            }
-        }
-        __syncthreads();
+        map_tile(p, tile, R, s_map);
         const int b = s_map[0];
         if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
 
@@ -556,6 +656,7 @@ struct Prefill {
         c.q_len = q_len_of(p, b);
         c.kv_len = kv_len_of(p, b);
         c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
+        c.causal = p.causal != 0;
         const int row0 = s_map[1] * R;
         const int hw = p.heads_per_wg;
         const int h = blockIdx.y * hw + (wave % hw);
@@ -567,15 +668,58 @@ struct Prefill {
         int kv_end = c.kv_len;
         if (p.causal) kv_end = min(kv_end, wg_last + c.diag + 1);
         kv_end = max(kv_end, 0);
-        c.ntiles = (kv_end + C::BN - 1) / C::BN;
+        c.t0 = 0;
+        c.t1 = (kv_end + C::BN - 1) / C::BN;
+        if (p.n_splits > 1) {  // split-KV: this workgroup takes one slice of the keys
+            const int per = p.split_keys / C::BN;
+            c.t0 = min((int)blockIdx.z * per, c.t1);
+            c.t1 = min(c.t0 + per, c.t1);
+        }
         const int wave_last = min(c.wr0 + 32, c.q_len) - 1;
         c.wave_kv_end = c.kv_len;
         if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
         c.kbase = (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * C::ES;
         c.vbase = (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * C::ES;
-        c.krs = make_rsrc(c.kbase, rows_bytes(c.kv_len, p.k.sn, D, C::ES));
-        c.vrs = make_rsrc(c.vbase, rows_bytes(c.kv_len, p.v.sn, D, C::ES));
+        c.kbytes = rows_bytes(c.kv_len, p.k.sn, D, C::ES);
+        c.vbytes = rows_bytes(c.kv_len, p.v.sn, D, C::ES);
+        c.ktile = (uint32_t)((int64_t)C::BN * p.k.sn * C::ES);
+        c.vtile = (uint32_t)((int64_t)C::BN * p.v.sn * C::ES);
+        {
+            const int ch = tid % C::CHUNKS, kg = tid / C::CHUNKS;
+#pragma unroll
+            for (int kk = 0; kk < C::KPT; ++kk) {
+                c.koff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.k.sn + ch * 8) * C::ES);
+                c.voff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.v.sn + ch * 8) * C::ES);
+            }
+        }
         c.mrow = nullptr;
+        c.mtile = nullptr;
+        c.mvalid = 0;
+        c.moff = 0;
+        c.mrow_l = -1;
+        c.mchunk = 0;
+        if (HAS_MASK && p.mask_lds) {
+            // 32 rows x BN keys; bool: 4 chunks of 16 B per row (threads
+            // 0..127), 16-bit: 8 chunks per row (all 256 threads).
+            const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
+            const int cpr = C::BN * es / 16;
+            if (tid < 32 * cpr) {
+                c.mrow_l = tid / cpr;
+                c.mchunk = tid % cpr;
+            }
+            c.mtile = (const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)row0 * p.m_si) * es;
+            const int rows = min(c.q_len - row0, 32);
+            // The window ends with the last valid row's keys rounded up to a
+            // whole 16-byte chunk (the mask's key extent is a multiple of 16
+            // bytes, so the rounded end stays inside that row): a partially
+            // valid chunk would otherwise be range-checked out as zeros.
+            const int64_t kend = ((int64_t)c.kv_len * es + 15) & ~(int64_t)15;
+            c.mvalid = rows > 0 && c.kv_len > 0
+                           ? (uint32_t)((int64_t)(rows - 1) * p.m_si * es + kend)
+                           : 0u;
+            c.moff = c.mrow_l >= 0 ? (uint32_t)((int64_t)c.mrow_l * p.m_si * es + c.mchunk * 16)
+                                   : 0xFFFFFFF0u;  // idle threads: out of range, no access
+        }
         if (HAS_MASK) {
             const int mes = p.mask_kind == MASK_BOOL ? 1 : (p.mask_kind == MASK_F32 ? 4 : 2);
             c.mrow = (const char*)p.mask +
@@ -635,6 +779,29 @@ struct Prefill {
         } else {
             sweep<PASS_ONLINE>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
             const float l_tot = l_run + __shfl_xor(l_run, 32);
+            if (p.n_splits > 1) {
+                // split-KV: unnormalized O with its reference max and sum
+                // (exp2 domain); the combine kernel merges the slices.
+                if (c.i < c.q_len) {
+                    const int64_t row = (p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q) + c.i;
+                    const int64_t slot = (row * p.hq + h) * p.n_splits + blockIdx.z;
+                    float* po = p.part_o + slot * D;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            f32x4 w;
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
+                            *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
+                        }
+                    if (lg == 0) {
+                        p.part_ml[slot * 2] = m_run;
+                        p.part_ml[slot * 2 + 1] = l_tot;
+                    }
+                }
+                return;
+            }
             factor *= l_tot > 0.f ? 1.f / l_tot : 0.f;
         }
 
@@ -658,18 +825,52 @@ struct Prefill {
 
 template <typename TI, int D, int MODE, bool HAS_MASK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * Cfg<TI, D>::STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[2 * Prefill<TI, D, HAS_MASK>::SSTAGE];
     Prefill<TI, D, HAS_MASK>::template run<MODE>(p, smem);
+}
+
+// Split-KV combine: one workgroup per (row tile, query head) merges the
+// key slices of each row with the log-sum-exp rule
+//   M = max m_s,  O = sum 2^(m_s - M) O_s / sum 2^(m_s - M) l_s
+// (exp2 domain) and writes the valid rows of Y.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
+    __shared__ int s_map[2];
+    const int R = p.rows_per_wg;
+    map_tile(p, blockIdx.x, R, s_map);
+    const int b = s_map[0];
+    if (b < 0) return;
+    const int h = blockIdx.y;
+    const int q_len = q_len_of(p, b);
+    const int row0 = s_map[1] * R;
+    const int S = p.n_splits;
+    const int64_t rbase = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
+    for (int e = threadIdx.x; e < R * D; e += 256) {
+        const int r = e / D, d = e % D, i = row0 + r;
+        if (i >= q_len) continue;
+        const int64_t slot0 = ((rbase + i) * p.hq + h) * S;
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, p.part_ml[(slot0 + sp) * 2]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f, acc = 0.f;
+        for (int sp = 0; sp < S; ++sp) {
+            const float f = fast_exp2(p.part_ml[(slot0 + sp) * 2] - Mu);
+            L += f * p.part_ml[(slot0 + sp) * 2 + 1];
+            acc += f * p.part_o[(slot0 + sp) * D + d];
+        }
+        const float y = L > 0.f ? acc / L * p.v_descale : 0.f;
+        TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+        orow[d] = (TO)y;
+    }
 }
 
 template <typename TI, int D, int MODE>
 static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
     if (p.mask_kind != MASK_NONE)
-        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, true>), dim3(grid_x, grid_y), dim3(256), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, true>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, false>), dim3(grid_x, grid_y), dim3(256), 0,
-                           stream, p);
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, false>), grid, dim3(256), 0, stream, p);
 }
 
 template <typename TI, int D>
@@ -681,8 +882,16 @@ static hipError_t launch_t(const AttnParams& p, int grid_x, int grid_y, hipStrea
         // fp8 Q/K/V always carry fp8 Q/DQ of the scores (host-checked)
         launch_m<TI, D, MODE_SOFTMAX_QDQ>(p, grid_x, grid_y, stream);
     } else {
-        if constexpr (!std::is_same<TI, fp8>::value)
+        if constexpr (!std::is_same<TI, fp8>::value) {
             launch_m<TI, D, MODE_SOFTMAX>(p, grid_x, grid_y, stream);
+            if (p.n_splits > 1) {
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                typedef typename std::conditional<std::is_same<TI, bf16>::value, bf16, f16>::type TO;
+                hipLaunchKernelGGL((prefill_combine_kernel<TO, D>), dim3(grid_x, p.hq), dim3(256), 0,
+                                   stream, p);
+            }
+        }
     }
     return hipGetLastError();
 }

@@ -6,6 +6,7 @@ sampled rows the oracle computes one by one.  Inputs are seeded and
 synthetic (gqa_attention_ragged_amd.synth); padding is NaN-poisoned, so a
 kernel that reads it produces NaN in a valid row.
 """
+import dataclasses
 import itertools
 
 import numpy as np
@@ -81,6 +82,31 @@ def test_masks(mask, causal, mask_heads):
               mask_heads=mask_heads)
     parity.compare(c, parity.run_gpu(c))
 
+
+
+@pytest.mark.parametrize("mask", ["bool", "f16", "bf16"])
+@pytest.mark.parametrize("causal", ["none", "lower_right", "upper_left"])
+@pytest.mark.parametrize("row_bcast", [False, True])
+def test_head_broadcast_masks_ragged_tails(mask, causal, row_bcast):
+    # Head-broadcast masks whose rows are whole 16-byte chunks (the kernel
+    # stages their tiles through LDS) with key lengths that end inside a
+    # chunk, and the last query row of each sequence at varied positions
+    # within a 32-row tile; row_bcast: one mask row shared by all queries.
+    seed = 250 + ["bool", "f16", "bf16"].index(mask) * 6 + ["none", "lower_right",
+                                                         "upper_left"].index(causal) * 2 + row_bcast
+    rng = np.random.default_rng(seed)
+    ql = np.array([31, 1, 70, 33, 17])
+    kl = rng.integers(1, 300, size=5) * 2 + 1  # odd lengths
+    if causal == "lower_right":
+        kl = np.maximum(kl, ql)
+    c = synth.generate(seed=seed, q_lens=ql, kv_lens=kl, num_heads=8, kv_num_heads=2,
+                       head_dim=128, query_form="packed_nhd", kv_form="padded_bhnd",
+                       n_kv=640, q_slack=2, kv_slack=0, dtype=torch.float16, mask_kind=mask,
+                       mask_p=0.2, mask_value=-3.0, mask_diag_true=True, causal_kind=causal,
+                       device=DEV, name=f"staged-mask-{mask}-{causal}-{row_bcast}")
+    if row_bcast:
+        c = dataclasses.replace(c, mask=c.mask[:, :, :1, :].contiguous())
+    parity.compare(c, parity.run_gpu(c))
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", [(4, 4), (8, 4), (8, 2), (8, 1), (12, 4), (6, 2)])
@@ -179,3 +205,26 @@ def test_workload_sampled(cfg):
         assert not torch.isnan(out[: int(np.sum(c.q_lens))].float()).any()
     else:
         assert not torch.isnan(out.float()).any()
+
+
+# ------------------------------------------------------------- split-KV prefill
+@pytest.mark.parametrize("causal,mask", [("lower_right", None), ("lower_right", "f16"),
+                                         ("none", "bool"), ("upper_left", None)])
+@pytest.mark.parametrize("dtype,D", [(torch.float16, 128), (torch.bfloat16, 64)])
+def test_split_kv_prefill(causal, mask, dtype, D):
+    # few query rows over long keys: the host splits the keys of each query
+    # tile over several workgroups and merges the partials
+    seed = 900 + D + ["lower_right", "none", "upper_left"].index(causal) * 3 + (mask is not None)
+    rng = np.random.default_rng(seed)
+    ql = np.array([37, 0, 5, 64])
+    kl = np.array([2900, 100, 5, 1500]) + rng.integers(0, 64, size=4)
+    if causal == "lower_right":
+        kl = np.maximum(kl, ql)
+    c = synth.generate(seed=seed, q_lens=ql, kv_lens=kl, num_heads=8, kv_num_heads=2,
+                       head_dim=D, query_form="packed_nhd", kv_form="padded_bhnd",
+                       n_kv=int(kl.max()) + 3, q_slack=2, dtype=dtype, mask_kind=mask,
+                       mask_p=0.2, mask_diag_true=True, causal_kind=causal, device=DEV,
+                       name=f"splitkv-{causal}-{mask}-{D}")
+    args = capi.make_args(c.q, c.k, c.v, c.mask, c.q, **c.kwargs())
+    assert capi.gqa_attn_workspace_size(args) > 0  # the split path is taken
+    parity.compare(c, parity.run_gpu(c))
