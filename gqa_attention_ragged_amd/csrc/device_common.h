@@ -127,13 +127,39 @@ __device__ __forceinline__ typename Vec8<T>::type e4m3x8_to(u32x2 w) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the two halves of the wave (lane l with lane l ^ 32)
+// with one v_permlane32_swap: of the two registers it returns, one holds the
+// lane's own value and the other its partner's, so their max / sum is the
+// pair's in every lane, without a round trip through LDS.
+__device__ __forceinline__ float halves_max(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const int a = r[0], b = r[1];  // copy out first: bit_cast of r[i] misreads the element
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const int a = r[0], b = r[1];
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
 // ---------------------------------------------------------------- buffer loads
 // A raw buffer resource over [base, base + bytes): loads whose range falls
 // outside return zero and touch no memory, so predicated tile loads need no
 // branches (branch-free loads also let the compiler count outstanding loads
 // exactly instead of draining them all).
+// `base` and `bytes` must be the same in every lane of the wave: they are
+// read from the first active lane into scalar registers, which keeps the
+// descriptor scalar (the compiler would otherwise wrap each load in a loop
+// over the distinct descriptors of the wave whenever it computed either value
+// with vector instructions).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+    const uint64_t a = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n,
                                              0x00020000);
 }
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4& v) {

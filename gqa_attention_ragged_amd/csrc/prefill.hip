@@ -556,14 +556,15 @@ struct Prefill {
                             eff = 1.f;
                         }
                     }
-                    float mx = -INFINITY;
+                    // row max over the lane's 32 scores: four independent chains
+                    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-                    mx *= eff;
+                        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+                    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * eff;
                     if (KIND != PASS_FIXED) {
-                        mx = fmaxf(mx, __shfl_xor(mx, 32));
+                        mx = halves_max(mx);
                         // Lazy rescaling: the reference max only moves when a
                         // row's max grows by more than 2^8, so exp2 values stay
                         // <= 256 and the O / l rescale is skipped for the wave
@@ -583,16 +584,16 @@ struct Prefill {
                             m_run = m_new;
                         }
                         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-                        float ls = 0.f;
+                        float l4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                             for (int r = 0; r < 16; ++r) {
                                 const float e = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
                                 s[kb][r] = e;
-                                ls += e;
+                                l4[r & 3] += e;
                             }
-                        l_run += ls;
+                        l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
                         if (KIND == PASS_ONLINE) bmm2_16(stage + C::KBYTES, s, o);
                     } else {
                         // reference max and sum known: P = exp2(s - m) / l,
@@ -648,7 +649,10 @@ struct Prefill {
         const int tile = gridDim.x - 1 - blockIdx.x;
 
         map_tile(p, tile, R, s_map);
-        const int b = s_map[0];
+        // (b, row tile) are workgroup-uniform: read them into scalar registers
+        // so that every address and buffer descriptor built from them is
+        // scalar too (a descriptor in vector registers needs a loop per load).
+        const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
         if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
 
         Ctx c;
@@ -657,7 +661,7 @@ struct Prefill {
         c.kv_len = kv_len_of(p, b);
         c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
         c.causal = p.causal != 0;
-        const int row0 = s_map[1] * R;
+        const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
         const int hw = p.heads_per_wg;
         const int h = blockIdx.y * hw + (wave % hw);
         const int kvh = (blockIdx.y * hw) / p.group;
@@ -772,13 +776,13 @@ struct Prefill {
             if (p.qdq) factor *= p.qscale;
         } else if constexpr (MODE == MODE_SOFTMAX_QDQ) {
             sweep<PASS_STATS>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
-            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            const float l_tot = halves_sum(l_run);
             const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
             sweep<PASS_FIXED>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
             factor *= p.qscale;
         } else {
             sweep<PASS_ONLINE>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
-            const float l_tot = l_run + __shfl_xor(l_run, 32);
+            const float l_tot = halves_sum(l_run);
             if (p.n_splits > 1) {
                 // split-KV: unnormalized O with its reference max and sum
                 // (exp2 domain); the combine kernel merges the slices.
