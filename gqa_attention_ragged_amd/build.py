@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "lib", "libgqa_attn.so")
-SOURCES = ["gqa_attn.cpp", "prefill.hip", "decode.hip"]
+SOURCES = ["gqa_attn.cpp", "prefill.hip", "prefill_pipe.hip", "decode.hip"]
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 

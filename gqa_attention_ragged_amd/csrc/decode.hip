@@ -95,7 +95,10 @@ struct Decode {
 
     __device__ __forceinline__ static void run(const AttnParams& p, char* smem) {
         const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+        const int tid = threadIdx.x, lane = tid & 63;
+        // wave index in a scalar register: everything derived from it is
+        // wave-uniform, and branches on it are scalar branches
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int l16 = lane & 15, g = lane >> 4;
         const int G = p.group;
         if (q_len_of(p, b) <= 0) return;

@@ -1,0 +1,72 @@
+// tile_common.h -- pieces shared by the prefill kernels: the ragged row-tile
+// map, the swizzled row-major V layout in LDS and the gfx950 LDS transpose
+// reads that turn it into MFMA operands.
+#pragma once
+#include "device_common.h"
+
+namespace gqa {
+
+// V is staged row-major; the 16-byte units of row `key` are XOR-swizzled so
+// that the transpose reads of one instruction (8 keys x 64 bytes for 16-bit
+// V, 16 keys x 32 bytes for fp8 V) spread evenly over the LDS banks.
+template <typename C>
+__device__ __forceinline__ int v_swz(int key) {
+    if constexpr (C::FP8) return 2 * ((key / C::RPL) % (C::VUNITS / 2));
+    else return 4 * ((key / C::RPL) % (C::VUNITS / 4));
+}
+// Byte offset of element d of V row `key`.
+template <typename C>
+__device__ __forceinline__ int v_addr(int key, int d) {
+    const int byte = d * C::ES;
+    return key * C::VROW + (((byte >> 4) ^ v_swz<C>(key)) << 4) + (byte & 15);
+}
+
+typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+// LDS transpose reads (gfx950): within each group of 16 lanes,
+// ds_read_b64_tr_b16 gives lane 4q+c the 16-bit element c of lanes 4k+q
+// (k = 0..3) and ds_read_b64_tr_b8 gives lane 8q+c the byte c of lanes 2k+q
+// (k = 0..7).  Pointing lane 4k+q (2k+q) at (key_k, d0 + 4q (8q)) of a
+// row-major V hands lane i the keys key_k at d = d0 + i: one row of V^T.
+__device__ __forceinline__ u32x2 tr16(const char* p) {
+    lds_h4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((__attribute__((address_space(3))) lds_h4*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x2 tr8(const char* p) {
+    return __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)p));
+}
+
+// ------------------------------------------------------------------ tile map
+// Row tile `tile` of the ragged batch -> (b, row tile within b), with the
+// tiles enumerated sequence by sequence (ceil(q_len_b / R) tiles each).
+// Wave 0 scans the per-sequence tile counts 64 sequences at a time; the
+// result lands in s_map[0..1] (b = -1 past the last tile).  Block-wide
+// barrier included.
+__device__ __forceinline__ void map_tile(const AttnParams& p, int tile, int R, int* s_map) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 0) {
+        if (lane == 0) s_map[0] = -1;
+        int acc = 0;
+        for (int base = 0; base < p.batch; base += 64) {
+            const int b = base + lane;
+            int n = 0;
+            if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
+            int incl = n;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int excl = incl - n;
+            if (n > 0 && tile >= acc + excl && tile < acc + incl) {
+                s_map[0] = b;
+                s_map[1] = tile - acc - excl;
+            }
+            acc += __shfl(incl, 63);
+            if (acc > tile) break;
+        }
+    }
+    __syncthreads();
+}
+
+}  // namespace gqa
