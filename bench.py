@@ -40,6 +40,8 @@ HBM_PEAK = 8000.0  # GB/s
 WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
+                "gqa_attention_ragged_amd/csrc/prefill_pipe.hip",
+                "gqa_attention_ragged_amd/csrc/tile_common.h",
                 "gqa_attention_ragged_amd/csrc/device_common.h"],
     "decode": ["gqa_attention_ragged_amd/csrc/decode.hip",
                "gqa_attention_ragged_amd/csrc/device_common.h"],
@@ -76,6 +78,17 @@ def work_of(case) -> dict:
         pairs += int(n.sum())
     pairs *= case.num_heads
     return {"kind": "prefill", "flop": 4 * D * pairs, "pairs": pairs}
+
+
+def kernel_name(case, kind: str) -> str:
+    """The kernel that dominates a step, as the library's planner picks it."""
+    import torch
+    if kind == "decode":
+        return "gqa::decode_split_kernel"
+    pipe = (case.q.dtype in (torch.float16, torch.bfloat16) and case.mask is None
+            and case.norm == "softmax" and not case.qdq and case.scale * case.k_descale > 0
+            and os.environ.get("GQA_ATTN_PREFILL") != "base")
+    return "gqa::prefill_pipe_kernel" if pipe else "gqa::prefill_kernel"
 
 
 def dtype_name(case) -> str:
@@ -233,6 +246,61 @@ def profile_pass(cfg: str) -> None:
     print(json.dumps({"profile_pass": cfg, "copy_bytes": n}), flush=True)
 
 
+def write_traffic(cfg: str, fetch_dir: str, write_dir: str) -> dict:
+    """profiles/traffic_cfg<cfg>.json from two rocprofv3 --pmc runs of
+    --profile-pass (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each
+    counter is scaled by what it reads for the 256 MiB device copy of the same
+    run, so that the figure is HBM bytes."""
+    import csv
+    import glob
+    from gqa_attention_ragged_amd import synth
+
+    def per_dispatch(d: str, counter: str) -> dict:
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+
+    case = synth.make_config(cfg, device="cpu")
+    kind = work_of(case)["kind"]
+    want = kernel_name(case, kind).split("::")[1]
+    out = {"workload": cfg}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        v = per_dispatch(d, counter)
+        ker = [(k, x) for k, x in v.items() if want in k[0]]
+        copy = [x for k, x in v.items() if "copyBuffer" in k[0] or "copy" in k[0].lower()]
+        if not ker or not copy:
+            raise SystemExit(f"{counter}: kernel or copy dispatch not found in {d}")
+        kib = sum(x for _, x in ker) / len(ker)
+        copy_kib = max(copy)
+        expect = (256 << 20) / 1024.0  # the copy reads and writes 256 MiB
+        scale = expect / copy_kib
+        tag = counter.split("_")[0].lower()
+        out["kernel"] = ker[0][0][0]
+        out[f"{tag}_kib_per_dispatch"] = kib
+        out[f"copy_256MiB_{tag}_kib"] = copy_kib
+        out[f"{tag}_scale"] = scale
+        out[f"{tag}_bytes"] = kib * 1024.0 * scale
+    out["kernel_sha"] = kernel_sha(kind)
+    out["hbm_bytes_per_launch"] = int(out["fetch_bytes"] + out["write_bytes"])
+    out["commands"] = [
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- "
+        f"python3 bench.py --profile-pass --workload {cfg}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- "
+        f"python3 bench.py --profile-pass --workload {cfg}",
+        f"python3 bench.py --write-traffic {fetch_dir} {write_dir} --workload {cfg}",
+    ]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    path = os.path.join(ROOT, "profiles", f"traffic_cfg{cfg}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,7 +311,11 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     a = ap.parse_args()
+    if a.write_traffic:
+        print(json.dumps(write_traffic(a.workload, *a.write_traffic)))
+        return 0
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {a.gpus} requested); the "
               "operator shards by KV-head group or by sequence with no exchange, but no "
@@ -267,7 +339,7 @@ def main() -> int:
     ach = main_r["value"]
     roof = {"bound": main_r["bound"], "achieved": ach, "peak": main_r["peak"],
             "unit": main_r["unit"], "frac": round(ach / main_r["peak"], 4), "traffic": traffic,
-            "kernel": "gqa::prefill_kernel" if kind == "prefill" else "gqa::decode_split_kernel",
+            "kernel": kernel_name(case, kind),
             "per_launch": per_launch}
     secondary = {}
     if not a.no_secondary:
