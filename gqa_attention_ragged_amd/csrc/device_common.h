@@ -114,14 +114,30 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
 }
 
 // Eight E4M3FN codes (two dwords) -> eight 16-bit values (exact: every
-// E4M3FN value is representable in f16 and bf16).
+// E4M3FN value is representable in f16 and bf16), two codes per
+// v_cvt_scalef32_pk_{f16,bf16}_fp8 with scale 1 (byte 2i -> element 2i).
+template <bool HI>
+__device__ __forceinline__ void e4m3x2_to(uint32_t w, f16& a, f16& b) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+    a = v[0];
+    b = v[1];
+}
+template <bool HI>
+__device__ __forceinline__ void e4m3x2_to(uint32_t w, bf16& a, bf16& b) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    a = v[0];
+    b = v[1];
+}
 template <typename T>
 __device__ __forceinline__ typename Vec8<T>::type e4m3x8_to(u32x2 w) {
     typename Vec8<T>::type r;
-    r[0] = (T)e4m3_to_f32<0>(w[0]); r[1] = (T)e4m3_to_f32<1>(w[0]);
-    r[2] = (T)e4m3_to_f32<2>(w[0]); r[3] = (T)e4m3_to_f32<3>(w[0]);
-    r[4] = (T)e4m3_to_f32<0>(w[1]); r[5] = (T)e4m3_to_f32<1>(w[1]);
-    r[6] = (T)e4m3_to_f32<2>(w[1]); r[7] = (T)e4m3_to_f32<3>(w[1]);
+    T x[8];
+    e4m3x2_to<false>(w[0], x[0], x[1]);
+    e4m3x2_to<true>(w[0], x[2], x[3]);
+    e4m3x2_to<false>(w[1], x[4], x[5]);
+    e4m3x2_to<true>(w[1], x[6], x[7]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = x[i];
     return r;
 }
 
