@@ -255,11 +255,11 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     }
 
     if (decode) {
-        // Keys per split: 512 (measured best at 128 x 8 heads x 32k keys, for
-        // fp16 and fp8 KV, against 256 .. 4096), halved while the grid has
+        // Keys per split: 4096 (measured best at 128 x 8 heads x 32k keys, for
+        // fp16 and fp8 KV, against 512 .. 8192), halved while the grid has
         // fewer than 4096 workgroups; GQA_ATTN_DECODE_SPLIT (a power of two,
         // 128..8192) overrides the start value for tuning.
-        int C = 512;
+        int C = 4096;
         if (const char* e = std::getenv("GQA_ATTN_DECODE_SPLIT")) {
             const int c = std::atoi(e);
             if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0) C = c;
@@ -267,7 +267,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         auto nsplit = [&](int c) { return (kv_max + c - 1) / c; };
         while (C > 128 && B * Hkv * nsplit(C) < 4096) C /= 2;
         const int64_t S = kv_max > 0 ? nsplit(C) : 1;
-        if (S > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many KV splits");
+        if (S > 65535) return fail(GQA_ERR_UNSUPPORTED, "too many KV splits");
+        if (B > 65535) return fail(GQA_ERR_UNSUPPORTED, "decode batch above 65535");
         p.split_keys = C;
         p.n_splits = (int)S;
         plan->kernel = K_DECODE;
