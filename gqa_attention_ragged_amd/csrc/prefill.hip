@@ -137,8 +137,15 @@ constexpr float kLazyRescale = 8.0f;  // log2 units
 // s_waitcnt immediate: vmcnt(0), expcnt / lgkmcnt not waited on.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-template <typename TI, int D, bool HAS_MASK>
+// Mask variants of the general kernel: none; read per lane from global memory
+// (any kind and layout); staged through LDS as 16-bit additive values -- f16
+// (an f16 mask, or a bool mask converted to 0 / -inf while staging) or bf16.
+enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3 };
+
+template <typename TI, int D, int MK>
 struct Prefill {
+    static constexpr bool HAS_MASK = MK != MK_NONE;
+    static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16;
     typedef Cfg<TI, D> C;
     typedef typename Chunk<TI>::type ChunkT;
     // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
@@ -172,6 +179,7 @@ struct Prefill {
         uint32_t mvalid;      // staged mask: bytes up to the last valid (row, key)
         uint32_t moff;        // staged mask: this thread's load offset in a tile
         int mrow_l, mchunk;   // staged mask: this thread's (row, 16-byte chunk); row < 0: idle
+        bool mbool;           // staged mask: bool source (converted to f16 0 / -inf)
         int i;                // this lane's query row
     };
 
@@ -193,8 +201,52 @@ struct Prefill {
             make_rsrc(c.mtile + off, c.mvalid > off ? c.mvalid - off : 0u);
         buf_load(mr, c.moff, rm);
     }
+    // Staged rows hold 16-bit additive values; a bool chunk (16 keys) becomes
+    // 16 f16 values, 0 (may attend) or -inf.
     __device__ __forceinline__ static void store_mask(char* stage, const Ctx& c, const u32x4& rm) {
-        if (c.mrow_l >= 0) *(u32x4*)(stage + C::STAGE + c.mrow_l * C::MROW + c.mchunk * 16) = rm;
+        if (c.mrow_l < 0) return;
+        char* row = stage + C::STAGE + c.mrow_l * C::MROW;
+        if (c.mbool) {
+            u32x4 h[2];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t b0 = (rm[w] >> (16 * half)) & 0xffu;
+                    const uint32_t b1 = (rm[w] >> (16 * half + 8)) & 0xffu;
+                    h[w >> 1][(w & 1) * 2 + half] = (b0 ? 0u : 0xFC00u) | (b1 ? 0u : 0xFC000000u);
+                }
+            *(u32x4*)(row + c.mchunk * 32) = h[0];
+            *(u32x4*)(row + c.mchunk * 32 + 16) = h[1];
+        } else {
+            *(u32x4*)(row + c.mchunk * 16) = rm;
+        }
+    }
+
+    // One staged additive mask value as float.
+    __device__ __forceinline__ static float staged_add(uint32_t h16) {
+        if constexpr (MK == MK_LDS_BF16) return __builtin_bit_cast(float, h16 << 16);
+        else return (float)__builtin_bit_cast(f16, (uint16_t)h16);
+    }
+
+    // Softmax on raw scores (scale > 0): the staged additive mask enters the
+    // raw domain as s + add / scale', so that exp2(s' * sc) carries
+    // add * log2 e; -inf removes the key.  kadd = log2 e / sc.
+    __device__ __forceinline__ static void apply_mask_raw(f32x16 (&s)[2], const char* stage,
+                                                          float kadd) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const u32x2 w = *(const u32x2*)(src + (kb * 32 + rq * 8 + lg * 4) * 2);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t h16 = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
+                    s[kb][rq * 4 + u] = __builtin_fmaf(staged_add(h16), kadd, s[kb][rq * 4 + u]);
+                }
+            }
     }
 
     __device__ __forceinline__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
@@ -266,8 +318,14 @@ struct Prefill {
     __device__ __forceinline__ static bool tile_is_full(const AttnParams& p, const Ctx& c, int tile,
                                                         float sc) {
         const int j0 = tile * C::BN;
-        return !HAS_MASK && j0 + C::BN <= c.kv_len && c.wr0 + 32 <= c.q_len &&
-               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag) && sc > 0.f;
+        return !HAS_MASK && cl_full(p, c, tile) && sc > 0.f;
+    }
+    // Whether the tile is fully allowed by the lengths and the causal rule
+    // (the mask aside) for every row of this wave.
+    __device__ __forceinline__ static bool cl_full(const AttnParams& p, const Ctx& c, int tile) {
+        const int j0 = tile * C::BN;
+        return j0 + C::BN <= c.kv_len && c.wr0 + 32 <= c.q_len &&
+               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag);
     }
 
     // Mask-free kernels: mark the keys a row may not see with -inf and keep
@@ -302,24 +360,15 @@ struct Prefill {
             for (int rq = 0; rq < 4; ++rq) {
                 const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
                 MaskGroup mg;
-                if (HAS_MASK && p.mask_lds) {
+                if constexpr (STAGED) {
                     // staged tile: row = this lane's row within the 32-row tile
                     const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
                     const int ko = kb * 32 + rq * 8 + lg * 4;
-                    if (p.mask_kind == MASK_BOOL) {
-                        const uint32_t w = *(const uint32_t*)(src + ko);
+                    const u32x2 w = *(const u32x2*)(src + ko * 2);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) { mg.ok[u] = (w >> (8 * u)) & 0xff; mg.add[u] = 0.f; }
-                    } else {
-                        const u32x2 w = *(const u32x2*)(src + ko * 2);
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const uint32_t h16 = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
-                            mg.add[u] = p.mask_kind == MASK_F16
-                                            ? (float)__builtin_bit_cast(f16, (uint16_t)h16)
-                                            : __builtin_bit_cast(float, h16 << 16);
-                            mg.ok[u] = true;
-                        }
+                    for (int u = 0; u < 4; ++u) {
+                        mg.add[u] = staged_add((w[u >> 1] >> ((u & 1) * 16)) & 0xffffu);
+                        mg.ok[u] = true;
                     }
                 } else if (HAS_MASK && row_ok) {
                     mg = load_mask_group(p, c.mrow, jg, c.kv_len);
@@ -333,7 +382,7 @@ struct Prefill {
                     const int r = rq * 4 + u;
                     bool a = row_ok && j < c.kv_len && (p.causal == 0 || j <= c.i + c.diag);
                     float v = s[kb][r] * sc;
-                    if (HAS_MASK && p.mask_kind == MASK_BOOL) {
+                    if (MK == MK_GENERIC && p.mask_kind == MASK_BOOL) {
                         a = a && mg.ok[u];
                     } else if (HAS_MASK) {
                         a = a && !(__builtin_isinf(mg.add[u]) && mg.add[u] < 0.f);
@@ -438,7 +487,7 @@ struct Prefill {
         const bool with_v = KIND != PASS_STATS;
         ChunkT rk[C::KPT], rv[C::KPT];
         u32x4 rm = {};
-        const bool mlds = HAS_MASK && p.mask_lds;
+        const bool mlds = STAGED;
         if (c.t0 < c.t1) {
             load_tile(p, c, c.t0, with_v, rk, rv);
             if (mlds) load_mask(p, c, c.t0, rm);
@@ -486,7 +535,12 @@ struct Prefill {
                     // into the exp2 argument (fma); otherwise the predicate
                     // scales them and marks disallowed keys with -inf.
                     float eff = sc;
-                    if (!tile_is_full(p, c, it, sc)) {
+                    if (STAGED && sc > 0.f) {
+                        // staged mask on raw scores, lengths / causal only
+                        // where the tile is not fully allowed
+                        apply_mask_raw(s, stage, ac / sc);
+                        if (!cl_full(p, c, it)) predicate_raw(c, it, s);
+                    } else if (!tile_is_full(p, c, it, sc)) {
                         if (!HAS_MASK && sc > 0.f) {
                             predicate_raw(c, it, s);
                         } else {
@@ -643,7 +697,8 @@ struct Prefill {
         c.moff = 0;
         c.mrow_l = -1;
         c.mchunk = 0;
-        if (HAS_MASK && p.mask_lds) {
+        c.mbool = p.mask_kind == MASK_BOOL;
+        if constexpr (STAGED) {
             // 32 rows x BN keys; bool: 4 chunks of 16 B per row (threads
             // 0..127), 16-bit: 8 chunks per row (all 256 threads).
             const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
@@ -768,10 +823,10 @@ struct Prefill {
     }
 };
 
-template <typename TI, int D, int MODE, bool HAS_MASK>
+template <typename TI, int D, int MODE, int MK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * Prefill<TI, D, HAS_MASK>::SSTAGE];
-    Prefill<TI, D, HAS_MASK>::template run<MODE>(p, smem);
+    __shared__ __attribute__((aligned(16))) char smem[2 * Prefill<TI, D, MK>::SSTAGE];
+    Prefill<TI, D, MK>::template run<MODE>(p, smem);
 }
 
 // Split-KV combine: one workgroup per (row tile, query head) merges the
@@ -812,10 +867,14 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
 template <typename TI, int D, int MODE>
 static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
-    if (p.mask_kind != MASK_NONE)
-        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, true>), grid, dim3(256), 0, stream, p);
+    if (p.mask_kind == MASK_NONE)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_NONE>), grid, dim3(256), 0, stream, p);
+    else if (!p.mask_lds)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_GENERIC>), grid, dim3(256), 0, stream, p);
+    else if (p.mask_kind == MASK_BF16)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS_BF16>), grid, dim3(256), 0, stream, p);
     else
-        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, false>), grid, dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS16>), grid, dim3(256), 0, stream, p);
 }
 
 template <typename TI, int D>
