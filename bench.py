@@ -40,6 +40,7 @@ HBM_PEAK = 8000.0  # GB/s
 WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
+                "gqa_attention_ragged_amd/csrc/prefill_impl.h",
                 "gqa_attention_ragged_amd/csrc/prefill_pipe.hip",
                 "gqa_attention_ragged_amd/csrc/tile_common.h",
                 "gqa_attention_ragged_amd/csrc/device_common.h"],

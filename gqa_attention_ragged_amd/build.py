@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "lib", "libgqa_attn.so")
-SOURCES = ["gqa_attn.cpp", "prefill.hip", "prefill_pipe.hip", "decode.hip"]
+SOURCES = ["gqa_attn.cpp", "prefill.hip", "prefill_f16.hip", "prefill_bf16.hip", "prefill_fp8.hip",
+           "prefill_pipe.hip", "decode.hip"]
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -55,7 +56,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     rt = _hip_runtime_dir()
     tmp = LIB + ".tmp%d" % os.getpid()

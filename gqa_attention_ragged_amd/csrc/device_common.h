@@ -47,6 +47,7 @@ struct AttnParams {
     int32_t causal;                   // 0 none, 1 upper_left, 2 lower_right
     int32_t norm_none;                // 1: TRT_normalization_op "none"
     int32_t qdq;                      // 0 off, 1 fp8, 2 int8
+    int32_t qdq_nosat;                // 1: P / qscale cannot leave the range (no clamp)
     float scale, qscale, k_descale, v_descale;
     int32_t hq, hkv, group;           // group = hq / hkv
     int32_t heads_per_wg, rows_per_wg;
@@ -106,6 +107,11 @@ __device__ __forceinline__ bf16 to_t(float x, bf16*) { return (bf16)x; }
 __device__ __forceinline__ uint32_t f32_to_e4m3_pair(float a, float b) {
     a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
     b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+// The same without the clamp, for inputs known to be in [0, 464): values in
+// [448, 464) still round to 448, only larger ones would become NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3_pair_unsat(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
 template <int BYTE>

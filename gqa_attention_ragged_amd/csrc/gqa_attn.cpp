@@ -237,6 +237,11 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     p.qdq = a->qdq;
     p.scale = a->scale;
     p.qscale = a->qdq ? a->qscale : 1.f;
+    // Softmax P <= 1, so x = P / qscale <= 1 / qscale (up to fp32 rounding):
+    // when that stays below the rounding limit of the format (fp8 E4M3FN: 464,
+    // int8: 127.5) the saturation of the quantizer can never act.
+    p.qdq_nosat = a->norm == GQA_NORM_SOFTMAX && a->qdq != GQA_QDQ_OFF && a->qscale > 0.f &&
+                  1.0 / (double)a->qscale <= (a->qdq == GQA_QDQ_FP8_E4M3 ? 460.0 : 127.0);
     p.k_descale = a->k_descale;
     p.v_descale = a->v_descale;
     p.hq = (int)Hq;

@@ -22,6 +22,14 @@ hipError_t launch_prefill_pipe(const AttnParams& p, int elem, int head_dim, int 
 hipError_t launch_prefill_combine(const AttnParams& p, int elem, int head_dim, int grid_x,
                                   hipStream_t stream);
 
+// The general prefill kernels of one element type (launch_prefill's parts).
+hipError_t launch_prefill_f16(const AttnParams& p, int head_dim, int grid_x, int grid_y,
+                              hipStream_t stream);
+hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid_x, int grid_y,
+                               hipStream_t stream);
+hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, int grid_x, int grid_y,
+                              hipStream_t stream);
+
 // Decode (query length 1) split-KV partial pass and its combine.
 // q_elem: Q type (f16/bf16); kv_elem: K/V type (same as q, or fp8).
 hipError_t launch_decode(const AttnParams& p, int q_elem, int kv_elem, int head_dim,

@@ -1,0 +1,913 @@
+// prefill_impl.h -- fused ragged GQA attention for query tiles (prefill, chunked
+// context, and any query length), gfx950.
+//
+// Computes, per valid query row, BMM1 -> causal / length / mask predicate ->
+// normalization (softmax or none) -> optional quantize-dequantize of the
+// normalized scores -> BMM2, as the onnx-tensorrt "TensorRT Custom Operator
+// Schemas" page defines TRT_Attention and TRT_QuantizedAttention.
+//
+// Work decomposition
+//   * A workgroup is 4 waves.  Each wave owns 32 query rows of one query
+//     head.  The waves of a workgroup share one KV head: with group size
+//     G = H_q / H_kv they cover HW = gcd(G, 4) heads of the same KV group and
+//     4 / HW blocks of 32 rows, so every K/V tile staged in LDS feeds 4 waves.
+//   * blockIdx.x enumerates query-row tiles over the whole ragged batch
+//     (sum_b ceil(q_len_b / rows_per_wg)); the tile -> (b, tile) map is
+//     rebuilt on the device from the cumulative lengths, so the host never
+//     reads device memory.  blockIdx.y enumerates head groups.
+//   * The key loop streams 64-key tiles through double-buffered LDS: K
+//     row-major, V transposed (V^T[d][key]) so that both MFMA operands are
+//     read with 16-byte LDS loads.
+//   * Scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles, so
+//     each lane owns one query row (lane % 32) and 16 of every 32 keys; the
+//     row max / sum need one exchange with lane ^ 32 only.  O is likewise
+//     accumulated transposed, O^T = V^T P^T.
+//   * Softmax runs online in the exp2 domain (scale * log2 e folded into the
+//     score scale), the published online-normalizer method (Milakov &
+//     Gimelshein 2018, as used by FlashAttention-2).  With Q/DQ the
+//     normalized P needs the final row max and sum, so a first pass over the
+//     keys computes them and a second pass quantizes exactly.
+//   * Padding is never read (loads are predicated on the valid lengths) and
+//     output rows are only written when they are valid.
+#pragma once
+#include "device_common.h"
+#include "launch.h"
+#include "tile_common.h"
+
+#include <type_traits>
+
+namespace gqa {
+
+template <typename TI, int D>
+struct Cfg {
+    static constexpr bool FP8 = std::is_same<TI, fp8>::value;
+    static constexpr int ES = FP8 ? 1 : 2;          // element bytes
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int KROW = D * ES + 16;        // LDS bytes per K row (padded)
+    static constexpr int VROW = D * ES;             // LDS bytes per V row (row-major, swizzled)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int VBYTES = BN * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int CHUNKS = D / 8;            // 8-element chunks per row
+    static constexpr int KPT = D / 32;              // keys per loader thread
+    static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
+    static constexpr int VUNITS = VROW / 16;        // 16-byte units per V row
+    static constexpr int RPL = VROW >= 256 ? 1 : 256 / VROW;  // V rows per 256-byte bank line
+    // Staged mask tile: 32 query rows x BN keys of a 1- or 2-byte mask
+    // (row stride padded by 16 bytes against bank conflicts).
+    static constexpr int MROW = BN * 2 + 16;
+    static constexpr int MBYTES = 32 * MROW;
+};
+
+template <typename TI>
+struct Chunk { typedef u32x4 type; };  // 8 x 16-bit
+template <>
+struct Chunk<fp8> { typedef u32x2 type; };  // 8 x 8-bit
+
+// Element e of an 8-element chunk, as raw bits.
+__device__ __forceinline__ uint32_t chunk_elem(u32x4 c, int e) {
+    return (c[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+}
+__device__ __forceinline__ uint32_t chunk_elem(u32x2 c, int e) {
+    return (c[e >> 2] >> ((e & 3) * 8)) & 0xffu;
+}
+
+// ------------------------------------------------------------------ mask
+struct MaskGroup {
+    float add[4];
+    bool ok[4];
+};
+
+__device__ __forceinline__ float mask_scalar(const AttnParams& p, const char* row, int64_t j) {
+    switch (p.mask_kind) {
+    case MASK_BOOL: return ((const uint8_t*)row)[j * p.m_sj] ? 1.f : 0.f;
+    case MASK_F16: return (float)((const f16*)row)[j * p.m_sj];
+    case MASK_BF16: return (float)((const bf16*)row)[j * p.m_sj];
+    default: return ((const float*)row)[j * p.m_sj];
+    }
+}
+
+// Mask values for keys jg..jg+3 of one row; keys >= kv_len are not read.
+__device__ __forceinline__ MaskGroup load_mask_group(const AttnParams& p, const char* row, int jg,
+                                                     int kv_len) {
+    MaskGroup m;
+    const bool is_bool = p.mask_kind == MASK_BOOL;
+    if (p.mask_vec && jg + 3 < kv_len) {
+        if (is_bool) {
+            uint32_t w = *(const uint32_t*)(row + (int64_t)jg);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { m.ok[u] = (w >> (8 * u)) & 0xff; m.add[u] = 0.f; }
+        } else if (p.mask_kind == MASK_F32) {
+            f32x4 w = *(const f32x4*)(row + (int64_t)jg * 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { m.add[u] = w[u]; m.ok[u] = true; }
+        } else {
+            u32x2 w = *(const u32x2*)(row + (int64_t)jg * 2);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                uint32_t h = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
+                if (p.mask_kind == MASK_F16) {
+                    m.add[u] = (float)__builtin_bit_cast(f16, (uint16_t)h);
+                } else {
+                    m.add[u] = __builtin_bit_cast(float, h << 16);
+                }
+                m.ok[u] = true;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            m.add[u] = 0.f;
+            m.ok[u] = false;
+            if (jg + u < kv_len) {
+                float x = mask_scalar(p, row, jg + u);
+                if (is_bool) m.ok[u] = x != 0.f;
+                else { m.add[u] = x; m.ok[u] = true; }
+            }
+        }
+    }
+    return m;
+}
+
+// ------------------------------------------------------------------ kernel
+enum PassKind { PASS_STATS = 0, PASS_ONLINE = 1, PASS_FIXED = 2, PASS_NONE = 3 };
+// Kernel modes: online softmax; softmax with Q/DQ of P (two passes);
+// "none" normalization (with or without Q/DQ).
+enum Mode { MODE_SOFTMAX = 0, MODE_SOFTMAX_QDQ = 1, MODE_NONE = 2, MODE_SOFTMAX_QDQ_NS = 3 };
+constexpr float kLazyRescale = 8.0f;  // log2 units
+// s_waitcnt immediate: vmcnt(0), expcnt / lgkmcnt not waited on.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Mask variants of the general kernel: none; read per lane from global memory
+// (any kind and layout); staged through LDS as 16-bit additive values -- f16
+// (an f16 mask, or a bool mask converted to 0 / -inf while staging) or bf16.
+enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3 };
+
+template <typename TI, int D, int MK>
+struct Prefill {
+    static constexpr bool HAS_MASK = MK != MK_NONE;
+    static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16;
+    typedef Cfg<TI, D> C;
+    typedef typename Chunk<TI>::type ChunkT;
+    // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
+    typedef typename std::conditional<C::FP8, f16, TI>::type T16;
+    typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
+
+    typedef typename Vec8<T16>::type V8;
+    // Bytes per pipeline stage: K tile, V tile and (mask kernels) a mask tile.
+    static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? C::MBYTES : 0);
+    // BMM1 B operand held in registers for the whole kernel: 8 x 16-bit
+    // values per k-step, or 32 E4M3FN codes per k-step.
+    typedef typename std::conditional<C::FP8, i32x8, V8>::type QOp;
+    typedef QOp QRegs[C::QSTEPS];
+    typedef f32x16 ORegs[D / 32];
+
+    // Per-workgroup state shared by the passes.
+    struct Ctx {
+        int b, q_len, kv_len, diag;
+        int t0, t1;           // key tiles [t0, t1) of this workgroup
+        bool causal;
+        int wr0;              // first row of this wave
+        bool wave_rows;       // wave has at least one valid row
+        int wave_kv_end;      // keys this wave can see (causal)
+        const char* kbase;    // K rows of (b, kv head)
+        const char* vbase;
+        uint32_t kbytes, vbytes;        // bytes from row 0 to the end of the last valid key
+        uint32_t ktile, vtile;          // bytes per tile of BN keys
+        uint32_t koff[C::KPT], voff[C::KPT];  // this thread's load offsets inside a tile
+        const char* mrow;     // mask row of this lane's query row (or null)
+        const char* mtile;    // staged mask: the workgroup's first mask row
+        uint32_t mvalid;      // staged mask: bytes up to the last valid (row, key)
+        uint32_t moff;        // staged mask: this thread's load offset in a tile
+        int mrow_l, mchunk;   // staged mask: this thread's (row, 16-byte chunk); row < 0: idle
+        bool mbool;           // staged mask: bool source (converted to f16 0 / -inf)
+        int i;                // this lane's query row
+    };
+
+    // A buffer window starting at tile `tile`: the wave-uniform base moves
+    // with the tile (scalar arithmetic only) and the range ends with the last
+    // valid key, so keys >= kv_len read as zero and touch no memory.
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t window(const char* base,
+                                                                    uint32_t valid,
+                                                                    uint32_t stride, int tile) {
+        const uint32_t off = (uint32_t)tile * stride;
+        return make_rsrc(base + off, valid > off ? valid - off : 0u);
+    }
+
+    __device__ __forceinline__ static void load_mask(const AttnParams& p, const Ctx& c, int tile,
+                                                     u32x4& rm) {
+        const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
+        const uint32_t off = (uint32_t)tile * (uint32_t)(C::BN * es);
+        const __amdgpu_buffer_rsrc_t mr =
+            make_rsrc(c.mtile + off, c.mvalid > off ? c.mvalid - off : 0u);
+        buf_load(mr, c.moff, rm);
+    }
+    // Staged rows hold 16-bit additive values; a bool chunk (16 keys) becomes
+    // 16 f16 values, 0 (may attend) or -inf.
+    __device__ __forceinline__ static void store_mask(char* stage, const Ctx& c, const u32x4& rm) {
+        if (c.mrow_l < 0) return;
+        char* row = stage + C::STAGE + c.mrow_l * C::MROW;
+        if (c.mbool) {
+            u32x4 h[2];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const uint32_t b0 = (rm[w] >> (16 * half)) & 0xffu;
+                    const uint32_t b1 = (rm[w] >> (16 * half + 8)) & 0xffu;
+                    h[w >> 1][(w & 1) * 2 + half] = (b0 ? 0u : 0xFC00u) | (b1 ? 0u : 0xFC000000u);
+                }
+            *(u32x4*)(row + c.mchunk * 32) = h[0];
+            *(u32x4*)(row + c.mchunk * 32 + 16) = h[1];
+        } else {
+            *(u32x4*)(row + c.mchunk * 16) = rm;
+        }
+    }
+
+    // One staged additive mask value as float.
+    __device__ __forceinline__ static float staged_add(uint32_t h16) {
+        if constexpr (MK == MK_LDS_BF16) return __builtin_bit_cast(float, h16 << 16);
+        else return (float)__builtin_bit_cast(f16, (uint16_t)h16);
+    }
+
+    // Softmax on raw scores (scale > 0): the staged additive mask enters the
+    // raw domain as s + add / scale', so that exp2(s' * sc) carries
+    // add * log2 e; -inf removes the key.  kadd = log2 e / sc.
+    __device__ __forceinline__ static void apply_mask_raw(f32x16 (&s)[2], const char* stage,
+                                                          float kadd) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const u32x2 w = *(const u32x2*)(src + (kb * 32 + rq * 8 + lg * 4) * 2);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t h16 = (w[u >> 1] >> ((u & 1) * 16)) & 0xffffu;
+                    s[kb][rq * 4 + u] = __builtin_fmaf(staged_add(h16), kadd, s[kb][rq * 4 + u]);
+                }
+            }
+    }
+
+    __device__ __forceinline__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
+                                     ChunkT (&rk)[C::KPT], ChunkT (&rv)[C::KPT]) {
+        (void)p;
+        const __amdgpu_buffer_rsrc_t kr = window(c.kbase, c.kbytes, c.ktile, tile);
+#pragma unroll
+        for (int kk = 0; kk < C::KPT; ++kk) buf_load(kr, c.koff[kk], rk[kk]);
+        if (with_v) {
+            const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
+#pragma unroll
+            for (int kk = 0; kk < C::KPT; ++kk) buf_load(vr, c.voff[kk], rv[kk]);
+        }
+    }
+
+    __device__ __forceinline__ static void store_tile(char* stage, bool with_v, const ChunkT (&rk)[C::KPT],
+                                      const ChunkT (&rv)[C::KPT]) {
+        const int t = threadIdx.x;
+        const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
+        char* sK = stage;
+        char* sV = stage + C::KBYTES;
+#pragma unroll
+        for (int kk = 0; kk < C::KPT; ++kk)
+            *(ChunkT*)(sK + (kg * C::KPT + kk) * C::KROW + ch * 8 * C::ES) = rk[kk];
+        if (!with_v) return;
+#pragma unroll
+        for (int kk = 0; kk < C::KPT; ++kk)
+            *(ChunkT*)(sV + v_addr<C>(kg * C::KPT + kk, ch * 8)) = rv[kk];
+    }
+
+    // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.  The
+    // two 32-key blocks accumulate in alternation so that consecutive MFMAs
+    // never wait on each other's result.
+    __device__ __forceinline__ static void bmm1(const char* sK, const QRegs& qreg, f32x16 (&s)[2]) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+        const char* row0 = sK + lr * C::KROW;
+        const char* row1 = sK + (32 + lr) * C::KROW;
+#pragma unroll
+        for (int ks = 0; ks < C::QSTEPS; ++ks) {
+            if constexpr (C::FP8) {
+                i32x8 a0, a1;
+                {
+                    const u32x4 lo = *(const u32x4*)(row0 + ks * 64 + lg * 32);
+                    const u32x4 hi = *(const u32x4*)(row0 + ks * 64 + lg * 32 + 16);
+                    a0[0] = lo[0]; a0[1] = lo[1]; a0[2] = lo[2]; a0[3] = lo[3];
+                    a0[4] = hi[0]; a0[5] = hi[1]; a0[6] = hi[2]; a0[7] = hi[3];
+                }
+                {
+                    const u32x4 lo = *(const u32x4*)(row1 + ks * 64 + lg * 32);
+                    const u32x4 hi = *(const u32x4*)(row1 + ks * 64 + lg * 32 + 16);
+                    a1[0] = lo[0]; a1[1] = lo[1]; a1[2] = lo[2]; a1[3] = lo[3];
+                    a1[4] = hi[0]; a1[5] = hi[1]; a1[6] = hi[2]; a1[7] = hi[3];
+                }
+                s[0] = mfma32_fp8(a0, qreg[ks], s[0]);
+                s[1] = mfma32_fp8(a1, qreg[ks], s[1]);
+            } else {
+                const V8 a0 = *(const V8*)(row0 + (ks * 16 + lg * 8) * 2);
+                const V8 a1 = *(const V8*)(row1 + (ks * 16 + lg * 8) * 2);
+                s[0] = mfma32(a0, qreg[ks], s[0]);
+                s[1] = mfma32(a1, qreg[ks], s[1]);
+            }
+        }
+    }
+
+    // Whether every (row, key) of this tile is allowed, so the raw scores can
+    // be used as they are (softmax folds the scale into its exp2 argument).
+    __device__ __forceinline__ static bool tile_is_full(const AttnParams& p, const Ctx& c, int tile,
+                                                        float sc) {
+        const int j0 = tile * C::BN;
+        return !HAS_MASK && cl_full(p, c, tile) && sc > 0.f;
+    }
+    // Whether the tile is fully allowed by the lengths and the causal rule
+    // (the mask aside) for every row of this wave.
+    __device__ __forceinline__ static bool cl_full(const AttnParams& p, const Ctx& c, int tile) {
+        const int j0 = tile * C::BN;
+        return j0 + C::BN <= c.kv_len && c.wr0 + 32 <= c.q_len &&
+               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag);
+    }
+
+    // Mask-free kernels: mark the keys a row may not see with -inf and keep
+    // the other raw scores (the scale is applied inside the exp2 argument).
+    // Key j of this lane's row is allowed iff j < lim, one compare per score.
+    __device__ __forceinline__ static void predicate_raw(const Ctx& c, int tile, f32x16 (&s)[2]) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        int lim = c.i < c.q_len ? c.kv_len : 0;
+        if (c.causal) lim = min(lim, c.i + c.diag + 1);
+        const int rel = lim - (tile * C::BN + lg * 4);  // key offset limit for this lane
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                s[kb][r] = off < rel ? s[kb][r] : -INFINITY;
+            }
+    }
+
+    // Scale the raw scores and apply the causal / length / mask predicate.
+    // Disallowed entries become -inf (softmax) or 0 (none).
+    __device__ __forceinline__ static void predicate(const AttnParams& p, const Ctx& c, int tile,
+                                                     f32x16 (&s)[2], float sc, float ac,
+                                                     bool none_norm, const char* stage) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        const int j0 = tile * C::BN;
+        const bool row_ok = c.i < c.q_len;
+        const float off = none_norm ? 0.f : -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
+                MaskGroup mg;
+                if constexpr (STAGED) {
+                    // staged tile: row = this lane's row within the 32-row tile
+                    const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+                    const int ko = kb * 32 + rq * 8 + lg * 4;
+                    const u32x2 w = *(const u32x2*)(src + ko * 2);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        mg.add[u] = staged_add((w[u >> 1] >> ((u & 1) * 16)) & 0xffffu);
+                        mg.ok[u] = true;
+                    }
+                } else if (HAS_MASK && row_ok) {
+                    mg = load_mask_group(p, c.mrow, jg, c.kv_len);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { mg.add[u] = 0.f; mg.ok[u] = true; }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = jg + u;
+                    const int r = rq * 4 + u;
+                    bool a = row_ok && j < c.kv_len && (p.causal == 0 || j <= c.i + c.diag);
+                    float v = s[kb][r] * sc;
+                    if (MK == MK_GENERIC && p.mask_kind == MASK_BOOL) {
+                        a = a && mg.ok[u];
+                    } else if (HAS_MASK) {
+                        a = a && !(__builtin_isinf(mg.add[u]) && mg.add[u] < 0.f);
+                        v += mg.add[u] * ac;
+                    }
+                    s[kb][r] = a ? v : off;
+                }
+            }
+        }
+    }
+
+    // BMM2 A operand for k-step ks (16 keys) and d-block db (32 values of d):
+    // lane (d = db*32 + lane%32, g = lane/32) gets keys
+    // ks*16 + (e/4)*8 + g*4 + e%4 for e = 0..7 -- the keys whose
+    // probabilities the same lane holds in its S^T accumulator.
+    __device__ __forceinline__ static V8 v_operand(const char* sV, int ks, int db) {
+        const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 5, dh = (lane >> 4) & 1;
+        const int d = db * 32 + dh * 16 + 4 * (l16 & 3);
+        const int key = ks * 16 + g * 4 + (l16 >> 2);
+        const u32x2 lo = tr16(sV + v_addr<C>(key, d));
+        const u32x2 hi = tr16(sV + v_addr<C>(key + 8, d));
+        u32x4 w;
+        w[0] = lo[0]; w[1] = lo[1]; w[2] = hi[0]; w[3] = hi[1];
+        return __builtin_bit_cast(V8, w);
+    }
+
+    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile.
+    __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            V8 b;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const V8 a = v_operand(sV, ks, db);
+                o[db] = mfma32(a, b, o[db]);
+            }
+        }
+    }
+
+    // "none" normalization keeps unbounded scores: split each into a 16-bit
+    // high part and a 16-bit remainder so BMM2 keeps ~fp32 accuracy.
+    __device__ __forceinline__ static void bmm2_16_split(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            V8 bh, bl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = pv[ks >> 1][(ks & 1) * 8 + e];
+                T16 h = to_t(x, (T16*)nullptr);
+                bh[e] = h;
+                bl[e] = to_t(x - (float)h, (T16*)nullptr);
+            }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const V8 a = v_operand(sV, ks, db);
+                o[db] = mfma32(a, bh, o[db]);
+                o[db] = mfma32(a, bl, o[db]);
+            }
+        }
+    }
+
+    // fp8 BMM2: P' codes (E4M3FN) against V^T codes, one 64-key k-step.
+    __device__ __forceinline__ static void bmm2_fp8(const char* sV, const i32x8& codes, ORegs& o) {
+        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            // four 8-key transpose reads; read t holds keys key(t, g, k)
+            const int l16 = lane & 15, dh = (lane >> 4) & 1, k = l16 >> 1;
+            const int d = db * 32 + dh * 16 + 8 * (l16 & 1);
+            i32x8 a;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int key = (t >> 1) * 32 + ((t & 1) * 2 + (k >> 2)) * 8 + lg * 4 + (k & 3);
+                const u32x2 w = tr8(sV + v_addr<C>(key, d));
+                a[2 * t] = (int)w[0];
+                a[2 * t + 1] = (int)w[1];
+            }
+            o[db] = mfma32_fp8(a, codes, o[db]);
+        }
+    }
+
+    // Quantize x (= P / qscale) and return the dequantized code value
+    // (without the qscale factor, which the epilogue applies).
+    template <bool SAT = true>
+    __device__ __forceinline__ static float qdq_value(float x, int kind) {
+        if (kind == 1) {
+            uint32_t code = SAT ? f32_to_e4m3_pair(x, 0.f) : f32_to_e4m3_pair_unsat(x, 0.f);
+            return e4m3_to_f32<0>(code);
+        }
+        float r = __builtin_rintf(x);
+        return SAT ? __builtin_amdgcn_fmed3f(r, -128.f, 127.f) : r;
+    }
+
+    // One sweep over the key tiles of this workgroup.
+    // SAT: the quantized scores may exceed the format's range and are
+    // saturated; without it the caller guarantees x = P / qscale stays below
+    // the rounding limit (P <= 1), and the clamp is left out.
+    template <int KIND, bool SAT = true>
+    __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c, char* smem,
+                                                 const QRegs& qreg, float sc, float ac,
+                                                 float& m_run, float& l_run, float inv, ORegs& o) {
+        const bool with_v = KIND != PASS_STATS;
+        ChunkT rk[C::KPT], rv[C::KPT];
+        u32x4 rm = {};
+        const bool mlds = STAGED;
+        if (c.t0 < c.t1) {
+            load_tile(p, c, c.t0, with_v, rk, rv);
+            if (mlds) load_mask(p, c, c.t0, rm);
+            store_tile(smem, with_v, rk, rv);
+            if (mlds) store_mask(smem, c, rm);
+        }
+        __syncthreads();
+        // Loop body for tile `it` computed from `stage` while tile it+1 is
+        // staged into `nstage`; unrolled by two below so that both stage
+        // addresses are compile-time LDS offsets.
+        auto body = [&](int it, char* stage, char* nstage) {
+            const bool more = it + 1 < c.t1;
+            if (more) load_tile(p, c, it + 1, with_v, rk, rv);
+            if (mlds && more) load_mask(p, c, it + 1, rm);
+            const int j0 = it * C::BN;
+            if (c.wave_rows && j0 < c.wave_kv_end) {
+                f32x16 s[2];
+                bmm1(stage, qreg, s);
+                if (KIND == PASS_NONE) {
+                    predicate(p, c, it, s, sc, ac, true, stage);
+                    if (p.qdq) {
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) s[kb][r] = qdq_value(s[kb][r] * inv, p.qdq);
+                        if constexpr (C::FP8) {
+                            i32x8 codes;
+#pragma unroll
+                            for (int w = 0; w < 8; ++w) {
+                                const int kb = w >> 2, r0 = (w & 3) * 4;
+                                uint32_t lo = f32_to_e4m3_pair(s[kb][r0], s[kb][r0 + 1]);
+                                uint32_t hi = f32_to_e4m3_pair(s[kb][r0 + 2], s[kb][r0 + 3]);
+                                codes[w] = (int)(lo | (hi << 16));
+                            }
+                            bmm2_fp8(stage + C::KBYTES, codes, o);
+                        } else {
+                            bmm2_16(stage + C::KBYTES, s, o);
+                        }
+                    } else {
+                        bmm2_16_split(stage + C::KBYTES, s, o);
+                    }
+                } else {
+                    // Softmax in the exp2 domain.  On a fully allowed tile the
+                    // raw dot products are kept and the score scale is folded
+                    // into the exp2 argument (fma); otherwise the predicate
+                    // scales them and marks disallowed keys with -inf.
+                    float eff = sc;
+                    if (STAGED && sc > 0.f) {
+                        // staged mask on raw scores, lengths / causal only
+                        // where the tile is not fully allowed
+                        apply_mask_raw(s, stage, ac / sc);
+                        if (!cl_full(p, c, it)) predicate_raw(c, it, s);
+                    } else if (!tile_is_full(p, c, it, sc)) {
+                        if (!HAS_MASK && sc > 0.f) {
+                            predicate_raw(c, it, s);
+                        } else {
+                            predicate(p, c, it, s, sc, ac, false, stage);
+                            eff = 1.f;
+                        }
+                    }
+                    // row max over the lane's 32 scores: four independent chains
+                    float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) m4[r & 3] = fmaxf(m4[r & 3], s[kb][r]);
+                    float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * eff;
+                    if (KIND != PASS_FIXED) {
+                        mx = halves_max(mx);
+                        // Lazy rescaling: the reference max only moves when a
+                        // row's max grows by more than 2^8, so exp2 values stay
+                        // <= 256 and the O / l rescale is skipped for the wave
+                        // on most tiles.  O / l is unchanged by the choice of
+                        // reference.
+                        const bool upd = mx > m_run + kLazyRescale;
+                        if (__any(upd)) {
+                            const float m_new = upd ? mx : m_run;
+                            const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+                            l_run *= alpha;
+                            if (KIND == PASS_ONLINE) {
+#pragma unroll
+                                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                                    for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+                            }
+                            m_run = m_new;
+                        }
+                        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+                        float l4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const float e = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
+                                s[kb][r] = e;
+                                l4[r & 3] += e;
+                            }
+                        l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+                        if (KIND == PASS_ONLINE) bmm2_16(stage + C::KBYTES, s, o);
+                    } else {
+                        // reference max and sum known: P = exp2(s - m) / l,
+                        // x = P / qscale = exp2(s - m) * inv = exp2(s - m')
+                        // with m' = m - log2(inv) (inv = 0: m' = +inf, x = 0)
+                        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+                        const float m_q = m_use - __builtin_amdgcn_logf(inv);
+                        if constexpr (C::FP8) {
+                            i32x8 codes;
+#pragma unroll
+                            for (int w = 0; w < 8; ++w) {
+                                const int kb = w >> 2, r0 = (w & 3) * 4;
+                                float x0 = fast_exp2(__builtin_fmaf(s[kb][r0], eff, -m_q));
+                                float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 1], eff, -m_q));
+                                float x2 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2], eff, -m_q));
+                                float x3 = fast_exp2(__builtin_fmaf(s[kb][r0 + 3], eff, -m_q));
+                                uint32_t lo = SAT ? f32_to_e4m3_pair(x0, x1) : f32_to_e4m3_pair_unsat(x0, x1);
+                                uint32_t hi = SAT ? f32_to_e4m3_pair(x2, x3) : f32_to_e4m3_pair_unsat(x2, x3);
+                                codes[w] = (int)(lo | (hi << 16));
+                            }
+                            bmm2_fp8(stage + C::KBYTES, codes, o);
+                        } else {
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r)
+                                    s[kb][r] = qdq_value<SAT>(
+                                        fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_q)), p.qdq);
+                            bmm2_16(stage + C::KBYTES, s, o);
+                        }
+                    }
+                }
+            }
+            if (more) store_tile(nstage, with_v, rk, rv);
+            if (mlds && more) store_mask(nstage, c, rm);
+            __syncthreads();
+        };
+        int it = c.t0;
+        for (; it + 1 < c.t1; it += 2) {
+            body(it, smem, smem + SSTAGE);
+            body(it + 1, smem + SSTAGE, smem);
+        }
+        if (it < c.t1) body(it, smem, smem + SSTAGE);
+    }
+
+    template <int MODE>
+    __device__ __forceinline__ static void run(const AttnParams& p, char* smem) {
+        __shared__ int s_map[2];
+        const int tid = threadIdx.x, lane = tid & 63;
+        // wave index in a scalar register: everything derived from it is
+        // wave-uniform, and branches on it are scalar branches
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lr = lane & 31, lg = lane >> 5;
+        const int R = p.rows_per_wg;
+        // Tiles are enumerated sequence by sequence, row tile by row tile; the
+        // workgroups take them in reverse so that, under causal masking, the
+        // heaviest (last) row tiles of each sequence are dispatched first.
+        const int tile = gridDim.x - 1 - blockIdx.x;
+
+        map_tile(p, tile, R, s_map);
+        // (b, row tile) are workgroup-uniform: read them into scalar registers
+        // so that every address and buffer descriptor built from them is
+        // scalar too (a descriptor in vector registers needs a loop per load).
+        const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
+        if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
+
+        Ctx c;
+        c.b = b;
+        c.q_len = q_len_of(p, b);
+        c.kv_len = kv_len_of(p, b);
+        c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
+        c.causal = p.causal != 0;
+        const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
+        const int hw = p.heads_per_wg;
+        const int h = blockIdx.y * hw + (wave % hw);
+        const int kvh = (blockIdx.y * hw) / p.group;
+        c.wr0 = row0 + (wave / hw) * 32;
+        c.i = c.wr0 + lr;
+        c.wave_rows = c.wr0 < c.q_len;
+        const int wg_last = min(row0 + R, c.q_len) - 1;
+        int kv_end = c.kv_len;
+        if (p.causal) kv_end = min(kv_end, wg_last + c.diag + 1);
+        kv_end = max(kv_end, 0);
+        c.t0 = 0;
+        c.t1 = (kv_end + C::BN - 1) / C::BN;
+        if (p.n_splits > 1) {  // split-KV: this workgroup takes one slice of the keys
+            const int per = p.split_keys / C::BN;
+            c.t0 = min((int)blockIdx.z * per, c.t1);
+            c.t1 = min(c.t0 + per, c.t1);
+        }
+        const int wave_last = min(c.wr0 + 32, c.q_len) - 1;
+        c.wave_kv_end = c.kv_len;
+        if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
+        c.kbase = (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * C::ES;
+        c.vbase = (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * C::ES;
+        c.kbytes = rows_bytes(c.kv_len, p.k.sn, D, C::ES);
+        c.vbytes = rows_bytes(c.kv_len, p.v.sn, D, C::ES);
+        c.ktile = (uint32_t)((int64_t)C::BN * p.k.sn * C::ES);
+        c.vtile = (uint32_t)((int64_t)C::BN * p.v.sn * C::ES);
+        {
+            const int ch = tid % C::CHUNKS, kg = tid / C::CHUNKS;
+#pragma unroll
+            for (int kk = 0; kk < C::KPT; ++kk) {
+                c.koff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.k.sn + ch * 8) * C::ES);
+                c.voff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.v.sn + ch * 8) * C::ES);
+            }
+        }
+        c.mrow = nullptr;
+        c.mtile = nullptr;
+        c.mvalid = 0;
+        c.moff = 0;
+        c.mrow_l = -1;
+        c.mchunk = 0;
+        c.mbool = p.mask_kind == MASK_BOOL;
+        if constexpr (STAGED) {
+            // 32 rows x BN keys; bool: 4 chunks of 16 B per row (threads
+            // 0..127), 16-bit: 8 chunks per row (all 256 threads).
+            const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
+            const int cpr = C::BN * es / 16;
+            if (tid < 32 * cpr) {
+                c.mrow_l = tid / cpr;
+                c.mchunk = tid % cpr;
+            }
+            c.mtile = (const char*)p.mask + ((int64_t)b * p.m_sb + (int64_t)row0 * p.m_si) * es;
+            const int rows = min(c.q_len - row0, 32);
+            // The window ends with the last valid row's keys rounded up to a
+            // whole 16-byte chunk (the mask's key extent is a multiple of 16
+            // bytes, so the rounded end stays inside that row): a partially
+            // valid chunk would otherwise be range-checked out as zeros.
+            const int64_t kend = ((int64_t)c.kv_len * es + 15) & ~(int64_t)15;
+            c.mvalid = rows > 0 && c.kv_len > 0
+                           ? (uint32_t)((int64_t)(rows - 1) * p.m_si * es + kend)
+                           : 0u;
+            c.moff = c.mrow_l >= 0 ? (uint32_t)((int64_t)c.mrow_l * p.m_si * es + c.mchunk * 16)
+                                   : 0xFFFFFFF0u;  // idle threads: out of range, no access
+        }
+        if (HAS_MASK) {
+            const int mes = p.mask_kind == MASK_BOOL ? 1 : (p.mask_kind == MASK_F32 ? 4 : 2);
+            c.mrow = (const char*)p.mask +
+                     ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)c.i * p.m_si) * mes;
+        }
+
+        // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg)
+        QRegs qreg;
+        {
+            const bool ok = c.i < c.q_len;
+            const char* qrow = (const char*)p.q.ptr +
+                               (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.i * p.q.sn) * C::ES;
+#pragma unroll
+            for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                if constexpr (C::FP8) {
+                    u32x4 lo = {}, hi = {};
+                    if (ok) {
+                        const u32x4* src = (const u32x4*)(qrow + ks * 64 + lg * 32);
+                        lo = src[0];
+                        hi = src[1];
+                    }
+                    i32x8 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                    qreg[ks] = a;
+                } else {
+                    V8 a = {};
+                    if (ok) a = *(const V8*)(qrow + (ks * 16 + lg * 8) * 2);
+                    qreg[ks] = a;
+                }
+            }
+            // Q must be resident before the key loop: otherwise the compiler
+            // cannot tell the Q loads from the K/V prefetch of the loop and
+            // waits for every outstanding load before the first MFMA.
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
+
+        ORegs o;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.f;
+        const bool none_norm = MODE == MODE_NONE;
+        const float sc = none_norm ? p.scale * p.k_descale : p.scale * p.k_descale * kLog2e;
+        const float ac = none_norm ? 1.f : kLog2e;
+        float factor = p.v_descale;
+
+        if constexpr (MODE == MODE_NONE) {
+            const float inv = p.qdq ? 1.f / p.qscale : 1.f;
+            sweep<PASS_NONE>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            if (p.qdq) factor *= p.qscale;
+        } else if constexpr (MODE == MODE_SOFTMAX_QDQ || MODE == MODE_SOFTMAX_QDQ_NS) {
+            sweep<PASS_STATS>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            const float l_tot = halves_sum(l_run);
+            const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
+            sweep<PASS_FIXED, MODE == MODE_SOFTMAX_QDQ>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            factor *= p.qscale;
+        } else {
+            sweep<PASS_ONLINE>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            const float l_tot = halves_sum(l_run);
+            if (p.n_splits > 1) {
+                // split-KV: unnormalized O with its reference max and sum
+                // (exp2 domain); the combine kernel merges the slices.
+                if (c.i < c.q_len) {
+                    const int64_t row = (p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q) + c.i;
+                    const int64_t slot = (row * p.hq + h) * p.n_splits + blockIdx.z;
+                    float* po = p.part_o + slot * D;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            f32x4 w;
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
+                            *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
+                        }
+                    if (lg == 0) {
+                        p.part_ml[slot * 2] = m_run;
+                        p.part_ml[slot * 2 + 1] = l_tot;
+                    }
+                }
+                return;
+            }
+            factor *= l_tot > 0.f ? 1.f / l_tot : 0.f;
+        }
+
+        // ---- epilogue: lane (row lr, group lg) holds O^T[d][row] for
+        // d = db*32 + rq*8 + lg*4 + u.
+        if (c.i < c.q_len) {
+            TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)c.i * p.o_sn;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    typedef TO TO4 __attribute__((ext_vector_type(4)));
+                    TO4 w;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) w[u] = to_t(o[db][rq * 4 + u] * factor, (TO*)nullptr);
+                    *(TO4*)(orow + db * 32 + rq * 8 + lg * 4) = w;
+                }
+        }
+    }
+};
+
+template <typename TI, int D, int MODE, int MK>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(16))) char smem[2 * Prefill<TI, D, MK>::SSTAGE];
+    Prefill<TI, D, MK>::template run<MODE>(p, smem);
+}
+
+// Split-KV combine: one workgroup per (row tile, query head) merges the
+// key slices of each row with the log-sum-exp rule
+//   M = max m_s,  O = sum 2^(m_s - M) O_s / sum 2^(m_s - M) l_s
+// (exp2 domain) and writes the valid rows of Y.
+template <typename TO, int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
+    __shared__ int s_map[2];
+    const int R = p.rows_per_wg;
+    map_tile(p, blockIdx.x, R, s_map);
+    const int b = s_map[0];
+    if (b < 0) return;
+    const int h = blockIdx.y;
+    const int q_len = q_len_of(p, b);
+    const int row0 = s_map[1] * R;
+    const int S = p.n_splits;
+    const int64_t rbase = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
+    for (int e = threadIdx.x; e < R * D; e += 256) {
+        const int r = e / D, d = e % D, i = row0 + r;
+        if (i >= q_len) continue;
+        const int64_t slot0 = ((rbase + i) * p.hq + h) * S;
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, p.part_ml[(slot0 + sp) * 2]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f, acc = 0.f;
+        for (int sp = 0; sp < S; ++sp) {
+            const float f = fast_exp2(p.part_ml[(slot0 + sp) * 2] - Mu);
+            L += f * p.part_ml[(slot0 + sp) * 2 + 1];
+            acc += f * p.part_o[(slot0 + sp) * D + d];
+        }
+        const float y = L > 0.f ? acc / L * p.v_descale : 0.f;
+        TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+        orow[d] = (TO)y;
+    }
+}
+
+template <typename TI, int D, int MODE>
+static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
+    if (p.mask_kind == MASK_NONE)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_NONE>), grid, dim3(256), 0, stream, p);
+    else if (!p.mask_lds)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_GENERIC>), grid, dim3(256), 0, stream, p);
+    else if (p.mask_kind == MASK_BF16)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS_BF16>), grid, dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS16>), grid, dim3(256), 0, stream, p);
+}
+
+template <typename TI, int D>
+static hipError_t launch_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    const int mode = p.norm_none ? MODE_NONE : (p.qdq ? MODE_SOFTMAX_QDQ : MODE_SOFTMAX);
+    if (mode == MODE_NONE) {
+        launch_m<TI, D, MODE_NONE>(p, grid_x, grid_y, stream);
+    } else if (mode == MODE_SOFTMAX_QDQ || std::is_same<TI, fp8>::value) {
+        // fp8 Q/K/V always carry fp8 Q/DQ of the scores (host-checked)
+        if (p.qdq_nosat)
+            launch_m<TI, D, MODE_SOFTMAX_QDQ_NS>(p, grid_x, grid_y, stream);
+        else
+            launch_m<TI, D, MODE_SOFTMAX_QDQ>(p, grid_x, grid_y, stream);
+    } else {
+        if constexpr (!std::is_same<TI, fp8>::value) {
+            launch_m<TI, D, MODE_SOFTMAX>(p, grid_x, grid_y, stream);
+            if (p.n_splits > 1) {
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                typedef typename std::conditional<std::is_same<TI, bf16>::value, bf16, f16>::type TO;
+                hipLaunchKernelGGL((prefill_combine_kernel<TO, D>), dim3(grid_x, p.hq), dim3(256), 0,
+                                   stream, p);
+            }
+        }
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gqa

@@ -27,7 +27,7 @@ def _lens(rng, B, lo, hi):
 
 def _case(seed, *, qf, kf, causal="none", mask=None, dtype=torch.float16, D=128, hq=8, hkv=2,
           norm="softmax", qdq=None, B=3, qmax=150, kvmax=170, zero=False, n_q_pad=None,
-          kv_fp8=False, mask_heads=1):
+          kv_fp8=False, mask_heads=1, qscale=None):
     rng = np.random.default_rng(seed)
     ql = _lens(rng, B, 0 if zero else 1, qmax)
     kl = _lens(rng, B, 0 if zero else 1, kvmax)
@@ -45,7 +45,8 @@ def _case(seed, *, qf, kf, causal="none", mask=None, dtype=torch.float16, D=128,
         kv_slack=2, pass_query_lengths=pass_ql, mask_kind=mask, mask_heads=mask_heads,
         mask_p=0.2, mask_value=-4.0 if seed % 3 else -float("inf"), mask_diag_true=True,
         causal_kind=causal, norm=norm, qdq=qdq,
-        qscale=float(np.float32(1 / 448.0)) if qdq == "fp8" else 1 / 64.0,
+        qscale=qscale if qscale is not None else (
+            float(np.float32(1 / 448.0)) if qdq == "fp8" else 1 / 64.0),
         kv_fp8_from=torch.float16 if kv_fp8 else None,
         kv_dtype=torch.float8_e4m3fn if kv_fp8 else None,
         dist="round_normal" if dtype == torch.float8_e4m3fn else "normal",
@@ -144,6 +145,19 @@ def test_fp8_quantized(causal, mask, D):
     c = _case(seed, qf="padded_bhnd", kf="padded_bhnd", causal=causal, mask=mask,
               dtype=torch.float8_e4m3fn, D=D, qdq="fp8", qmax=200, kvmax=200)
     parity.compare(c, parity.run_gpu(c))
+
+
+@pytest.mark.parametrize("dtype,qdq,qscale", [
+    (torch.float8_e4m3fn, "fp8", 1 / 2000.0), (torch.float16, "fp8", 1 / 1000.0),
+    (torch.bfloat16, "int8", 1 / 400.0), (torch.float8_e4m3fn, "fp8", 1 / 460.0)])
+def test_qdq_saturating_scales(dtype, qdq, qscale):
+    # small qscale: P / qscale exceeds the format's range on the largest
+    # probabilities and the quantizer saturates (the kernel keeps its clamp);
+    # 1/460 is the largest range the clamp-free variant accepts
+    seed = 650 + int(1 / qscale) % 97
+    c = _case(seed, qf="padded_bhnd", kf="padded_bhnd", causal="upper_left", dtype=dtype,
+              qdq=qdq, qscale=float(np.float32(qscale)), qmax=120, kvmax=120, B=2)
+    parity.compare(c, parity.run_gpu(c), amb_rel=1e-4)
 
 
 @pytest.mark.parametrize("kv", ["f16", "bf16", "fp8"])
