@@ -69,51 +69,5 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int tile, int R, i
     __syncthreads();
 }
 
-// Row tile `idx` in longest-first order: the tiles of all sequences are
-// enumerated by their position t within the sequence, last position first
-// (t = T-1 .. 0, T = the largest tile count), and at one position by
-// sequence.  Under causal masking a tile's key range grows with t, so the
-// heaviest tiles of every sequence start first and the light ones fill the
-// tail of the grid.  Wave 0 counts, per position, the sequences that reach
-// it (ballots over 64 sequences at a time); the result lands in s_map[0..1]
-// (b = -1 past the last tile).  Block-wide barrier included.
-__device__ __forceinline__ void map_tile_lpt(const AttnParams& p, int idx, int R, int* s_map) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if (wave == 0) {
-        if (lane == 0) s_map[0] = -1;
-        // T = max over sequences of the tile count
-        int tmax = 0;
-        for (int base = 0; base < p.batch; base += 64) {
-            const int b = base + lane;
-            const int n = b < p.batch ? (q_len_of(p, b) + R - 1) / R : 0;
-            int m = n;
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
-            tmax = max(tmax, m);
-        }
-        int rem = idx;
-        for (int t = tmax - 1; t >= 0 && rem >= 0; --t) {
-            for (int base = 0; base < p.batch; base += 64) {
-                const int b = base + lane;
-                const int n = b < p.batch ? (q_len_of(p, b) + R - 1) / R : 0;
-                const unsigned long long bal = __ballot(n > t);
-                const int cnt = __popcll(bal);
-                if (rem < cnt) {
-                    // the rem-th set bit of the ballot
-                    const unsigned long long below =
-                        lane == 0 ? 0ull : (bal & (~0ull >> (64 - lane)));
-                    if ((n > t) && __popcll(below) == rem) {
-                        s_map[0] = b;
-                        s_map[1] = t;
-                    }
-                    rem = -1;
-                    break;
-                }
-                rem -= cnt;
-            }
-        }
-    }
-    __syncthreads();
-}
 
 }  // namespace gqa
