@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # dense MFMA TFLOP/s
 HBM_PEAK = 8000.0  # GB/s
-WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "1")
+WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "kvu", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
                 "gqa_attention_ragged_amd/csrc/prefill_impl.h",
@@ -135,9 +135,38 @@ def time_steps(step, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / steps
 
 
+def measure_kv_update(steps: int, warmup: int) -> dict:
+    """The KV-cache update workload: bytes = update rows read + cache rows
+    written (all rows land inside the cache)."""
+    import torch
+    from gqa_attention_ragged_amd import capi, synth
+    c = synth.make_kv_update_workload(device="cuda")
+    args = capi.make_kv_update_args(c.past_cache, c.update, **c.kwargs())
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = capi.load()
+    import ctypes
+    pargs = ctypes.byref(args)
+
+    def step():
+        st = lib.gqa_kv_cache_update(pargs, stream)
+        if st != 0:
+            raise capi.GqaError(st, capi.last_error())
+
+    ms = time_steps(step, steps, warmup)
+    H, D = c.past_cache.shape[1], c.past_cache.shape[3]
+    byts = 2 * int(np.sum(c.counts)) * H * D * c.past_cache.element_size()
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"workload": "kvu", "description": synth.KV_UPDATE_DESCRIPTION, "ms_per_step": round(ms, 4),
+            "dtype": "bf16", "metric": "KV-cache update GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "bytes": byts, "roofline_frac": round(gbs / HBM_PEAK, 4), "bound": "hbm",
+            "peak": HBM_PEAK, "_case": c}
+
+
 def measure(cfg: str, steps: int, warmup: int) -> dict:
     import torch
     from gqa_attention_ragged_amd import synth
+    if cfg == "kvu":
+        return measure_kv_update(steps, warmup)
     case = synth.make_config(cfg, device="cuda")
     torch.cuda.synchronize()
     w = work_of(case)
@@ -310,7 +339,7 @@ def main() -> int:
     # the default warm-up covers that, so the timed steps are steady state.
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=150)
-    ap.add_argument("--workload", default="2", choices=WORKLOADS)
+    ap.add_argument("--workload", default="2", choices=[w for w in WORKLOADS if w != "kvu"])
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

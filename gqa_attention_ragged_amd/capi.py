@@ -66,6 +66,18 @@ class GqaArgs(ctypes.Structure):
     ]
 
 
+class GqaKvUpdateArgs(ctypes.Structure):
+    """gqa_kv_update_args_t (include/gqa_kv_cache.h)."""
+    _fields_ = [
+        ("past_cache", GqaTensor),
+        ("update", GqaTensor),
+        ("out", GqaTensor),
+        ("write_indices", ctypes.c_void_p),
+        ("update_lengths", ctypes.c_void_p),
+        ("update_form", ctypes.c_int32),
+    ]
+
+
 class GqaError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"gqa_attn: {status_str(status)} ({status}): {detail}")
@@ -99,6 +111,11 @@ def load() -> ctypes.CDLL:
         lib.gqa_attn_last_hip_error.restype = ctypes.c_int
         lib.gqa_attn_abi_version.argtypes = []
         lib.gqa_attn_abi_version.restype = ctypes.c_int
+        K = ctypes.POINTER(GqaKvUpdateArgs)
+        lib.gqa_kv_cache_update_validate.argtypes = [K]
+        lib.gqa_kv_cache_update_validate.restype = ctypes.c_int
+        lib.gqa_kv_cache_update.argtypes = [K, ctypes.c_void_p]
+        lib.gqa_kv_cache_update.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -208,3 +225,42 @@ def attn_forward(q, k, v, attn_mask=None, *, out=None, workspace=None, stream=No
         stream = torch.cuda.current_stream(q.device).cuda_stream
     gqa_attn_forward(args, workspace if n else None, stream)
     return out
+
+
+# ------------------------------------------------------------ KV-cache update
+def make_kv_update_args(past_cache, update, out=None, *, write_indices=None, update_lengths=None,
+                        update_form="padded_bhnd") -> GqaKvUpdateArgs:
+    """gqa_kv_update_args_t for torch tensors (out = past_cache: in place)."""
+    a = GqaKvUpdateArgs()
+    a.past_cache = tensor_view(past_cache)
+    a.update = tensor_view(update)
+    a.out = tensor_view(past_cache if out is None else out)
+    a.write_indices = None if write_indices is None else write_indices.data_ptr()
+    a.update_lengths = None if update_lengths is None else update_lengths.data_ptr()
+    a.update_form = FORMS[update_form]
+    a._keep = (past_cache, update, out, write_indices, update_lengths)
+    return a
+
+
+def gqa_kv_cache_update_validate(args: GqaKvUpdateArgs) -> int:
+    return load().gqa_kv_cache_update_validate(ctypes.byref(args))
+
+
+def gqa_kv_cache_update(args: GqaKvUpdateArgs, stream) -> None:
+    st = load().gqa_kv_cache_update(ctypes.byref(args), stream)
+    if st != GQA_OK:
+        raise GqaError(st, last_error())
+
+
+def kv_cache_update(past_cache, update, *, out=None, write_indices=None, update_lengths=None,
+                    update_form="padded_bhnd", stream=None):
+    """Y = TRT_KVCacheUpdate(past_cache, update, ...) on the current torch
+    stream; in place (Y is past_cache) unless ``out`` is given."""
+    if not past_cache.is_cuda:
+        raise ValueError("kv_cache_update runs on the GPU: pass device tensors")
+    args = make_kv_update_args(past_cache, update, out, write_indices=write_indices,
+                               update_lengths=update_lengths, update_form=update_form)
+    if stream is None:
+        stream = torch.cuda.current_stream(past_cache.device).cuda_stream
+    gqa_kv_cache_update(args, stream)
+    return past_cache if out is None else out

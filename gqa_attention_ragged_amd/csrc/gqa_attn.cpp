@@ -4,6 +4,7 @@
 // The host never reads device memory: every geometry decision uses shapes
 // only (T, B, N, H), and the kernels resolve the ragged lengths themselves.
 #include "gqa_attn.h"
+#include "gqa_kv_cache.h"
 
 #include <hip/hip_runtime.h>
 
@@ -413,10 +414,101 @@ const char* gqa_attn_status_str(int status) {
     return "unknown status";
 }
 
+// ------------------------------------------------------------ KV-cache update
+namespace {
+
+int plan_kv_update(const gqa_kv_update_args_t* a, gqa::KvUpdateParams* p) {
+    if (!a) return fail(GQA_ERR_INVALID_ARG, "args is null");
+    if (a->update_form != GQA_FORM_PADDED_BHND && a->update_form != GQA_FORM_PACKED_NHD)
+        return fail(GQA_ERR_INVALID_ARG, "update_form must be 0 or 1");
+    int st;
+    if ((st = check_tensor(a->past_cache, "past_cache", GQA_FORM_PADDED_BHND))) return st;
+    if ((st = check_tensor(a->update, "update", a->update_form))) return st;
+    if ((st = check_tensor(a->out, "out", GQA_FORM_PADDED_BHND))) return st;
+    const gqa_tensor_t &c = a->past_cache, &u = a->update, &y = a->out;
+    const int dt = c.dtype;
+    if (dt != GQA_DT_F16 && dt != GQA_DT_BF16 && dt != GQA_DT_FP8_E4M3)
+        return fail(GQA_ERR_INVALID_ARG, "past_cache dtype must be f16, bf16 or fp8 e4m3");
+    if (u.dtype != dt || y.dtype != dt)
+        return fail(GQA_ERR_INVALID_ARG, "update and out must have past_cache's dtype");
+    const int64_t B = c.shape[0], H = c.shape[1], N = c.shape[2], D = c.shape[3];
+    for (int d = 0; d < 4; ++d)
+        if (y.shape[d] != c.shape[d]) return fail(GQA_ERR_INVALID_ARG, "out must have past_cache's shape");
+    const bool packed = a->update_form == GQA_FORM_PACKED_NHD;
+    if (packed) {
+        if (u.shape[1] != H || u.shape[2] != D)
+            return fail(GQA_ERR_INVALID_ARG, "packed update must be [T, H, D] with the cache's H and D");
+        if (!a->update_lengths)
+            return fail(GQA_ERR_INVALID_ARG, "a packed update needs update_lengths");
+    } else {
+        if (u.shape[0] != B || u.shape[1] != H || u.shape[3] != D)
+            return fail(GQA_ERR_INVALID_ARG, "padded update must be [B, H, N_u, D] with the cache's B, H, D");
+    }
+    const int es = elem_bytes(dt);
+    if ((D * es) % 16) return fail(GQA_ERR_UNSUPPORTED, "D * element size must be a multiple of 16 bytes");
+    if (B > INT32_MAX || H > INT32_MAX || N > INT32_MAX || (!packed && u.shape[2] > INT32_MAX))
+        return fail(GQA_ERR_UNSUPPORTED, "extent above 2^31");
+    const bool same = y.data == c.data;
+    if (same)
+        for (int d = 0; d < 4; ++d)
+            if (y.stride[d] != c.stride[d])
+                return fail(GQA_ERR_INVALID_ARG, "out aliases past_cache with different strides");
+    *p = gqa::KvUpdateParams{};
+    p->upd = (const char*)u.data;
+    if (packed) {
+        p->u_sb = 0;
+        p->u_sh = u.stride[1];
+        p->u_sn = u.stride[0];
+        p->T = u.shape[0];
+    } else {
+        p->u_sb = u.stride[0];
+        p->u_sh = u.stride[1];
+        p->u_sn = u.stride[2];
+        p->n_u = (int32_t)u.shape[2];
+    }
+    p->cache = (const char*)c.data;
+    p->c_sb = c.stride[0];
+    p->c_sh = c.stride[1];
+    p->c_sn = c.stride[2];
+    p->out = (char*)y.data;
+    p->o_sb = y.stride[0];
+    p->o_sh = y.stride[1];
+    p->o_sn = y.stride[2];
+    p->wi = a->write_indices;
+    p->ul = a->update_lengths;
+    p->packed = packed;
+    p->B = (int32_t)B;
+    p->H = (int32_t)H;
+    p->N = (int32_t)N;
+    p->es = es;
+    p->row_bytes = (int32_t)(D * es);
+    p->in_place = same;
+    return GQA_OK;
+}
+
+}  // namespace
+
+int gqa_kv_cache_update_validate(const gqa_kv_update_args_t* args) {
+    gqa::KvUpdateParams p;
+    return plan_kv_update(args, &p);
+}
+
+int gqa_kv_cache_update(const gqa_kv_update_args_t* args, void* stream) {
+    gqa::KvUpdateParams p;
+    const int st = plan_kv_update(args, &p);
+    if (st != GQA_OK) return st;
+    const hipError_t e = gqa::launch_kv_update(p, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_hip_err = (int)e;
+        return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
+    return GQA_OK;
+}
+
 const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_last_hip_error(void) { return g_hip_err; }
 
-int gqa_attn_abi_version(void) { return 1; }
+int gqa_attn_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -35,4 +35,27 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, int grid_x, int
 hipError_t launch_decode(const AttnParams& p, int q_elem, int kv_elem, int head_dim,
                          hipStream_t stream);
 
+// KV-cache update (TRT_KVCacheUpdate, linear mode).  Element strides; the
+// row of (b, h, n) of the cache / output starts at base + b*sb + h*sh + n*sn
+// elements; the packed update row r of head h at base + r*sn + h*sh.
+struct KvUpdateParams {
+    const char* upd;
+    int64_t u_sb, u_sh, u_sn;
+    const char* cache;
+    int64_t c_sb, c_sh, c_sn;
+    char* out;
+    int64_t o_sb, o_sh, o_sn;
+    const int32_t* wi;   // write indices [B] or null
+    const int32_t* ul;   // cumulative update lengths [B+1] or null
+    int32_t packed;
+    int32_t B, H, N;     // cache extents
+    int32_t n_u;         // padded update rows per sequence
+    int64_t T;           // packed update rows
+    int32_t es;          // element bytes
+    int32_t row_bytes;   // D * es, a multiple of 16
+    int32_t in_place;    // out is the cache: copy nothing but the update rows
+};
+
+hipError_t launch_kv_update(const KvUpdateParams& p, hipStream_t stream);
+
 }  // namespace gqa

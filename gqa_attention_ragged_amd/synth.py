@@ -323,3 +323,68 @@ def make_config(cfg: str, device="cpu") -> Case:
                     qdq="fp8", qscale=float(np.float32(1.0 / 448.0)), pass_kv_lengths=False,
                     mask_kind="bool" if cfg == "5b" else None, mask_p=0.1, mask_diag_true=True,
                     device=device, name="cfg" + cfg)
+
+
+# ------------------------------------------------------------ KV-cache update
+@dataclass
+class KvUpdateCase:
+    name: str
+    past_cache: torch.Tensor            # [B, H, N, D]
+    update: torch.Tensor                # padded [B, H, N_u, D] or packed [T, H, D]
+    write_indices: Optional[torch.Tensor]
+    update_lengths: Optional[torch.Tensor]
+    update_form: str
+    counts: np.ndarray                  # rows each sequence writes (before dropping)
+    starts: np.ndarray                  # write index of each sequence
+
+    def kwargs(self) -> dict:
+        return dict(write_indices=self.write_indices, update_lengths=self.update_lengths,
+                    update_form=self.update_form)
+
+
+def kv_update_case(*, seed: int, B: int, H: int, N: int, D: int, counts, starts=None,
+                   update_form: str = "padded_bhnd", dtype=torch.float16, pass_lengths=True,
+                   pass_indices=True, n_u=None, slack: int = 0, device="cpu",
+                   name: str = "kvu") -> KvUpdateCase:
+    """A seeded cache and update: counts[b] rows for sequence b written from
+    starts[b] (drawn in [0, N - counts[b]] when None).  Padded updates carry
+    NaN-free random rows everywhere (rows past counts[b] must not be used);
+    packed updates carry `slack` extra rows at the end."""
+    rng = np.random.default_rng(seed)
+    counts = np.asarray(counts, dtype=np.int64)
+    if starts is None:
+        starts = np.array([int(rng.integers(0, max(N - c, 0) + 1)) for c in counts], dtype=np.int64)
+    starts = np.asarray(starts, dtype=np.int64)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def rand(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return x.to(dtype)
+
+    cache = rand((B, H, N, D))
+    if update_form == "packed_nhd":
+        upd = rand((int(counts.sum()) + slack, H, D))
+    else:
+        nu = int(counts.max(initial=0)) if n_u is None else n_u
+        upd = rand((B, H, nu, D))
+    ul = None
+    if pass_lengths or update_form == "packed_nhd":
+        ul = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device=device)
+    wi = torch.tensor(starts, dtype=torch.int32, device=device) if pass_indices else None
+    return KvUpdateCase(name=name, past_cache=cache, update=upd, write_indices=wi, update_lengths=ul,
+                        update_form=update_form, counts=counts,
+                        starts=starts if pass_indices else np.zeros(B, np.int64))
+
+
+KV_UPDATE_DESCRIPTION = ("KV-cache update, packed bf16 rows of 16 sequences L~U[64,2048] written "
+                         "in place into a padded [16, 8, 4096, 128] cache at random offsets")
+
+
+def make_kv_update_workload(device="cpu") -> KvUpdateCase:
+    """The prefill workload's K written into a cache: 16 sequences, lengths of
+    the prefill workload, H=8, D=128, bf16, cache length 4096."""
+    q_lens, _ = config_lengths("2")
+    return kv_update_case(seed=21, B=16, H=8, N=4096, D=128, counts=q_lens,
+                          update_form="packed_nhd", dtype=torch.bfloat16, device=device,
+                          name="kvu")

@@ -155,7 +155,8 @@ const char* gqa_attn_last_error(void);
 /* The hipError_t of the last GQA_ERR_HIP on this thread (0 if none). */
 int gqa_attn_last_hip_error(void);
 
-/* Library ABI version (bumped on any change of these declarations). */
+/* Library ABI version (bumped on any change of these declarations or of
+ * those in gqa_kv_cache.h; 2 adds the KV-cache update). */
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

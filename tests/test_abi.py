@@ -11,24 +11,26 @@ import pytest
 from gqa_attention_ragged_amd import capi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 F16, BF16, FP8, F32, BOOL = 0, 1, 2, 3, 4
 PADDED, PACKED = 0, 1
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gqa_attn_\w+)\s*\(", text, re.M)))
+    text = "".join(open(h).read() for h in HEADERS)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gqa_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
     lib = capi.load()
     names = declared_functions()
-    assert len(names) >= 7, names
+    assert len(names) >= 9, names
+    assert "gqa_kv_cache_update" in names and "gqa_kv_cache_update_validate" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 1
+    assert lib.gqa_attn_abi_version() == 2
 
 
 _addr = [0x100000]
@@ -166,3 +168,47 @@ def test_empty_batch_is_valid():
     a.q.shape[0] = 0
     a.out.shape[0] = 0
     assert st(a) == capi.GQA_OK
+
+
+# ------------------------------------------------------------ KV-cache update
+def kv_args(form=PADDED, B=2, H=4, N=64, D=128, nu=8, T=10, dt=F16, in_place=True):
+    a = capi.GqaKvUpdateArgs()
+    a.past_cache = fake([B, H, N, D], dt)
+    a.update = fake([B, H, nu, D] if form == PADDED else [T, H, D], dt)
+    a.out = a.past_cache if in_place else fake([B, H, N, D], dt)
+    a.write_indices = 0x7000
+    a.update_lengths = 0x8000
+    a.update_form = form
+    return a
+
+
+@pytest.mark.parametrize("form", [PADDED, PACKED])
+@pytest.mark.parametrize("dt", [F16, BF16, FP8])
+@pytest.mark.parametrize("in_place", [True, False])
+def test_kv_update_validate_accepts(form, dt, in_place):
+    a = kv_args(form=form, dt=dt, in_place=in_place)
+    assert capi.gqa_kv_cache_update_validate(a) == 0, capi.last_error()
+
+
+def test_kv_update_validate_rejects():
+    a = kv_args(form=PACKED)
+    a.update_lengths = None
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # packed needs lengths
+    a = kv_args()
+    a.update.dtype = BF16
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # dtype mismatch
+    a = kv_args()
+    a.update.shape[1] = 3
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # head count mismatch
+    a = kv_args(in_place=False)
+    a.out.shape[2] = 63
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # out shape
+    a = kv_args(dt=FP8, D=8)
+    assert capi.gqa_kv_cache_update_validate(a) == 2  # 8-byte rows
+    a = kv_args()
+    a.out = fake([2, 4, 64, 128], F16)
+    a.out.data = a.past_cache.data
+    a.out.stride[0] = a.past_cache.stride[0] * 2
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # aliasing with other strides
+    a = kv_args(dt=F32)
+    assert capi.gqa_kv_cache_update_validate(a) == 1  # dtype

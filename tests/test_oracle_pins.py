@@ -300,7 +300,7 @@ def test_fully_masked_rows_are_zero(oracle_mod):
 def _load_golden():
     out = []
     for fn in sorted(os.listdir(GOLDEN)):
-        if fn.endswith(".json"):
+        if fn.startswith("attention") and fn.endswith(".json"):
             with open(os.path.join(GOLDEN, fn)) as f:
                 for case in json.load(f)["cases"]:
                     out.append(pytest.param(case, id=f"{fn[:-5]}:{case['name']}"))
