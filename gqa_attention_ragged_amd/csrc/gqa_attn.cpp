@@ -327,10 +327,19 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // Concurrent workgroups: one 8-wave workgroup per CU for the pipelined
     // kernel, two 4-wave ones for the general kernel (256 CUs).
     const int64_t slots = plan->pipe && plan->pipe_waves == 8 ? 256 : 512;
+    // Splitting only pays while the workgroups cannot fill the GPU once: the
+    // fp32 partials cost rows * H_q * S * (D + 2) * 4 bytes written and read
+    // again (measured on the chunked-context workload, 576 workgroups: no
+    // split 449 TFLOP/s, 6 slices 358).
     if (a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF && qdt != GQA_DT_FP8_E4M3 &&
-        wgs < 3 * slots && kv_tiles >= 8) {
-        int64_t S = (6 * slots + wgs - 1) / wgs;
-        S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));
+        wgs < slots && kv_tiles >= 8) {
+        int64_t S = (2 * slots + wgs - 1) / wgs;
+        S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
+        // GQA_ATTN_PREFILL_SPLITS (1..32) overrides the slice count for tuning
+        if (const char* e = std::getenv("GQA_ATTN_PREFILL_SPLITS")) {
+            const int v = std::atoi(e);
+            if (v >= 1 && v <= 32) S = std::min<int64_t>(v, std::max<int64_t>(kv_tiles, 1));
+        }
         if (S > 1) {
             const int64_t per_tiles = (kv_tiles + S - 1) / S;
             S = (kv_tiles + per_tiles - 1) / per_tiles;

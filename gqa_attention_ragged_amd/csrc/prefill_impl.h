@@ -842,32 +842,45 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
 // (exp2 domain) and writes the valid rows of Y.
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
+    // One wave per (row, head) at a time: lane s holds slice s's (m, l)
+    // (S <= 64), the wave reduces M and L, then each lane sums its d values
+    // over the slices with the weights broadcast from their lanes.
     __shared__ int s_map[2];
     const int R = p.rows_per_wg;
     map_tile(p, blockIdx.x, R, s_map);
-    const int b = s_map[0];
+    const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
     if (b < 0) return;
     const int h = blockIdx.y;
     const int q_len = q_len_of(p, b);
-    const int row0 = s_map[1] * R;
+    const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
     const int S = p.n_splits;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t rbase = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
-    for (int e = threadIdx.x; e < R * D; e += 256) {
-        const int r = e / D, d = e % D, i = row0 + r;
-        if (i >= q_len) continue;
+    for (int r = wave; r < R; r += 4) {
+        const int i = row0 + r;
+        if (i >= q_len) break;
         const int64_t slot0 = ((rbase + i) * p.hq + h) * S;
-        float M = -INFINITY;
-        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, p.part_ml[(slot0 + sp) * 2]);
+        const float m = lane < S ? p.part_ml[(slot0 + lane) * 2] : -INFINITY;
+        const float l = lane < S ? p.part_ml[(slot0 + lane) * 2 + 1] : 0.f;
+        float M = m;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
         const float Mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f, acc = 0.f;
-        for (int sp = 0; sp < S; ++sp) {
-            const float f = fast_exp2(p.part_ml[(slot0 + sp) * 2] - Mu);
-            L += f * p.part_ml[(slot0 + sp) * 2 + 1];
-            acc += f * p.part_o[(slot0 + sp) * D + d];
-        }
-        const float y = L > 0.f ? acc / L * p.v_descale : 0.f;
+        const float w = lane < S ? fast_exp2(m - Mu) : 0.f;
+        float L = w * l;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+        const float inv = L > 0.f ? p.v_descale / L : 0.f;
         TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
-        orow[d] = (TO)y;
+        for (int d = lane; d < D; d += 64) {
+            float acc = 0.f;
+            for (int sp = 0; sp < S; ++sp) {
+                const float ws = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), sp));
+                acc += ws * p.part_o[(slot0 + sp) * D + d];
+            }
+            orow[d] = (TO)(acc * inv);
+        }
     }
 }
 
