@@ -41,7 +41,6 @@ WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "kvu", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
                 "gqa_attention_ragged_amd/csrc/prefill_impl.h",
-                "gqa_attention_ragged_amd/csrc/prefill_pipe.hip",
                 "gqa_attention_ragged_amd/csrc/tile_common.h",
                 "gqa_attention_ragged_amd/csrc/device_common.h"],
     "decode": ["gqa_attention_ragged_amd/csrc/decode.hip",
@@ -82,14 +81,8 @@ def work_of(case) -> dict:
 
 
 def kernel_name(case, kind: str) -> str:
-    """The kernel that dominates a step, as the library's planner picks it."""
-    import torch
-    if kind == "decode":
-        return "gqa::decode_split_kernel"
-    pipe = (case.q.dtype in (torch.float16, torch.bfloat16) and case.mask is None
-            and case.norm == "softmax" and not case.qdq and case.scale * case.k_descale > 0
-            and os.environ.get("GQA_ATTN_PREFILL") != "base")
-    return "gqa::prefill_pipe_kernel" if pipe else "gqa::prefill_kernel"
+    """The kernel that dominates a step."""
+    return "gqa::decode_split_kernel" if kind == "decode" else "gqa::prefill_kernel"
 
 
 def dtype_name(case) -> str:

@@ -52,8 +52,6 @@ enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2 };
 
 struct Plan {
     Kernel kernel = K_NONE;
-    bool pipe = false;  // prefill on the software-pipelined kernel
-    int pipe_waves = 4;  // its waves per workgroup
     gqa::AttnParams p{};
     int q_elem = 0, kv_elem = 0, head_dim = 0;
     int grid_x = 0, grid_y = 0;
@@ -282,18 +280,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         return GQA_OK;
     }
 
-    // The software-pipelined kernel covers 16-bit Q/K/V with softmax, no Q/DQ,
-    // no mask and a positive score scale; GQA_ATTN_PREFILL=base forces the
-    // general kernel (for comparisons).
-    const char* force = std::getenv("GQA_ATTN_PREFILL");
-    plan->pipe = a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
-                 (qdt == GQA_DT_F16 || qdt == GQA_DT_BF16) && !m.data &&
-                 a->scale * a->k_descale > 0.f && !(force && std::strcmp(force, "base") == 0);
-    const char* pw = std::getenv("GQA_ATTN_PIPE_WAVES");
-    plan->pipe_waves = pw && std::atoi(pw) == 8 ? 8 : 4;
-    const int rg = plan->pipe ? plan->pipe_waves : 4;  // 32-row groups per workgroup
-    const int hw = gcd((int)G, rg);
-    const int R = 32 * (rg / hw);
+    const int hw = gcd((int)G, 4);
+    const int R = 32 * (4 / hw);
     p.heads_per_wg = hw;
     p.rows_per_wg = R;
     // Mask tiles shared by a workgroup's heads are staged through LDS when the
@@ -324,9 +312,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // for online softmax (Q/DQ needs the full row before quantizing).
     const int64_t wgs = (int64_t)plan->grid_x * plan->grid_y;
     const int64_t kv_tiles = (kv_max + 63) / 64;
-    // Concurrent workgroups: one 8-wave workgroup per CU for the pipelined
-    // kernel, two 4-wave ones for the general kernel (256 CUs).
-    const int64_t slots = plan->pipe && plan->pipe_waves == 8 ? 256 : 512;
+    // Concurrent workgroups: two 4-wave workgroups per CU (256 CUs).
+    const int64_t slots = 512;
     // Splitting only pays while the workgroups cannot fill the GPU once: the
     // fp32 partials cost rows * H_q * S * (D + 2) * 4 bytes written and read
     // again (measured on the chunked-context workload, 576 workgroups: no
@@ -395,15 +382,7 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
             plan.p.part_o = (float*)w;
             plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
         }
-        if (plan.pipe) {
-            e = gqa::launch_prefill_pipe(plan.p, plan.q_elem, plan.head_dim, plan.pipe_waves,
-                                         plan.grid_x, plan.grid_y, s);
-            if (e == hipSuccess && plan.p.n_splits > 1)
-                e = gqa::launch_prefill_combine(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, s);
-        } else {
-            e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y,
-                                    s);
-        }
+        e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
     }
     if (e != hipSuccess) {
         g_hip_err = (int)e;

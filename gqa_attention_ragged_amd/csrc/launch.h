@@ -13,12 +13,7 @@ enum Elem { ELEM_F16 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2 };
 hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
                           hipStream_t stream);
 
-// Software-pipelined prefill for 16-bit Q/K/V, softmax, no Q/DQ, no mask,
-// score scale > 0: `waves` (4 or 8) row groups of 32 rows per workgroup,
-// heads_per_wg = gcd(G, waves), rows_per_wg = 32 * waves / heads_per_wg.  The
-// split-KV combine (when n_splits > 1) is launched by launch_prefill_combine.
-hipError_t launch_prefill_pipe(const AttnParams& p, int elem, int head_dim, int waves, int grid_x,
-                               int grid_y, hipStream_t stream);
+// Split-KV combine of the prefill kernel (when n_splits > 1).
 hipError_t launch_prefill_combine(const AttnParams& p, int elem, int head_dim, int grid_x,
                                   hipStream_t stream);
 

@@ -243,14 +243,3 @@ def test_split_kv_prefill(causal, mask, dtype, D):
     assert capi.gqa_attn_workspace_size(args) > 0  # the split path is taken
     parity.compare(c, parity.run_gpu(c))
 
-
-# ------------------------------------------------- general kernel, forced
-@pytest.mark.parametrize("causal", ["none", "upper_left", "lower_right"])
-@pytest.mark.parametrize("dtype,D", [(torch.float16, 128), (torch.bfloat16, 64)])
-def test_general_kernel_forced(monkeypatch, causal, dtype, D):
-    # mask-free softmax cases normally run on the software-pipelined kernel;
-    # the general kernel must give the same results when forced
-    monkeypatch.setenv("GQA_ATTN_PREFILL", "base")
-    seed = 950 + D + ["none", "upper_left", "lower_right"].index(causal)
-    c = _case(seed, qf="packed_nhd", kf="padded_bhnd", causal=causal, dtype=dtype, D=D)
-    parity.compare(c, parity.run_gpu(c))
