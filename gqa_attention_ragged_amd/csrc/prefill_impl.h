@@ -48,8 +48,14 @@ struct Cfg {
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = BN * VROW;
     static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int CHUNKS = D / 8;            // 8-element chunks per row
-    static constexpr int KPT = D / 32;              // keys per loader thread
+    // K / V tiles are copied HBM -> LDS by buffer loads that write LDS
+    // directly, 1 KiB (64 lanes x 16 bytes, contiguous) per instruction; the
+    // 4 waves take the instructions of a tile round-robin.
+    static constexpr int NKD = KBYTES / 1024;       // instructions per K tile
+    static constexpr int NVD = VBYTES / 1024;       // instructions per V tile
+    static constexpr int KMAX = (NKD + 3) / 4;      // per wave, at most
+    static constexpr int VMAX = (NVD + 3) / 4;
+    static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "tiles copy in whole KiB");
     static constexpr int QSTEPS = FP8 ? D / 64 : D / 16;  // BMM1 k-steps
     static constexpr int VUNITS = VROW / 16;        // 16-byte units per V row
     static constexpr int RPL = VROW >= 256 ? 1 : 256 / VROW;  // V rows per 256-byte bank line
@@ -58,11 +64,6 @@ struct Cfg {
     static constexpr int MROW = BN * 2 + 16;
     static constexpr int MBYTES = 32 * MROW;
 };
-
-template <typename TI>
-struct Chunk { typedef u32x4 type; };  // 8 x 16-bit
-template <>
-struct Chunk<fp8> { typedef u32x2 type; };  // 8 x 8-bit
 
 // Element e of an 8-element chunk, as raw bits.
 __device__ __forceinline__ uint32_t chunk_elem(u32x4 c, int e) {
@@ -148,7 +149,6 @@ struct Prefill {
     static constexpr bool HAS_MASK = MK != MK_NONE;
     static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16;
     typedef Cfg<TI, D> C;
-    typedef typename Chunk<TI>::type ChunkT;
     // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
     typedef typename std::conditional<C::FP8, f16, TI>::type T16;
     typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
@@ -174,7 +174,7 @@ struct Prefill {
         const char* vbase;
         uint32_t kbytes, vbytes;        // bytes from row 0 to the end of the last valid key
         uint32_t ktile, vtile;          // bytes per tile of BN keys
-        uint32_t koff[C::KPT], voff[C::KPT];  // this thread's load offsets inside a tile
+        uint32_t koff[C::KMAX], voff[C::VMAX];  // this lane's source offsets inside a tile
         const char* mrow;     // mask row of this lane's query row (or null)
         const char* mtile;    // staged mask: the workgroup's first mask row
         uint32_t mvalid;      // staged mask: bytes up to the last valid (row, key)
@@ -250,32 +250,29 @@ struct Prefill {
             }
     }
 
-    __device__ __forceinline__ static void load_tile(const AttnParams& p, const Ctx& c, int tile, bool with_v,
-                                     ChunkT (&rk)[C::KPT], ChunkT (&rv)[C::KPT]) {
-        (void)p;
+    // Start the copy of tile `tile` (K, and V when with_v) into `stage`:
+    // instruction j of the tile writes LDS bytes [j KiB, j KiB + 1 KiB) of the
+    // K (V) region, lane i the 16 bytes at i * 16, read from the source offset
+    // the lane was given for that position (padding lanes of K get an offset
+    // beyond the range: zeros, no memory access).  Completion is waited for
+    // with vmcnt before the barrier that publishes the stage.
+    __device__ __forceinline__ static void dma_tile(const Ctx& c, int tile, bool with_v,
+                                                    char* stage, int wave) {
         const __amdgpu_buffer_rsrc_t kr = window(c.kbase, c.kbytes, c.ktile, tile);
 #pragma unroll
-        for (int kk = 0; kk < C::KPT; ++kk) buf_load(kr, c.koff[kk], rk[kk]);
-        if (with_v) {
-            const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
-#pragma unroll
-            for (int kk = 0; kk < C::KPT; ++kk) buf_load(vr, c.voff[kk], rv[kk]);
+        for (int k = 0; k < C::KMAX; ++k) {
+            const int j = wave + 4 * k;
+            if (j < C::NKD)
+                buf_load_lds16(kr, stage + j * 1024, c.koff[k]);
         }
-    }
-
-    __device__ __forceinline__ static void store_tile(char* stage, bool with_v, const ChunkT (&rk)[C::KPT],
-                                      const ChunkT (&rv)[C::KPT]) {
-        const int t = threadIdx.x;
-        const int ch = t % C::CHUNKS, kg = t / C::CHUNKS;
-        char* sK = stage;
-        char* sV = stage + C::KBYTES;
-#pragma unroll
-        for (int kk = 0; kk < C::KPT; ++kk)
-            *(ChunkT*)(sK + (kg * C::KPT + kk) * C::KROW + ch * 8 * C::ES) = rk[kk];
         if (!with_v) return;
+        const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
 #pragma unroll
-        for (int kk = 0; kk < C::KPT; ++kk)
-            *(ChunkT*)(sV + v_addr<C>(kg * C::KPT + kk, ch * 8)) = rv[kk];
+        for (int k = 0; k < C::VMAX; ++k) {
+            const int j = wave + 4 * k;
+            if (j < C::NVD)
+                buf_load_lds16(vr, stage + C::KBYTES + j * 1024, c.voff[k]);
+        }
     }
 
     // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.  The
@@ -486,26 +483,27 @@ struct Prefill {
     // saturated; without it the caller guarantees x = P / qscale stays below
     // the rounding limit (P <= 1), and the clamp is left out.
     template <int KIND, bool SAT = true>
-    __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c, char* smem,
+    __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c,
+                                                 char* __restrict__ st0, char* __restrict__ st1,
                                                  const QRegs& qreg, float sc, float ac,
                                                  float& m_run, float& l_run, float inv, ORegs& o) {
         const bool with_v = KIND != PASS_STATS;
-        ChunkT rk[C::KPT], rv[C::KPT];
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         u32x4 rm = {};
         const bool mlds = STAGED;
         if (c.t0 < c.t1) {
-            load_tile(p, c, c.t0, with_v, rk, rv);
+            dma_tile(c, c.t0, with_v, st0, wave);
             if (mlds) load_mask(p, c, c.t0, rm);
-            store_tile(smem, with_v, rk, rv);
-            if (mlds) store_mask(smem, c, rm);
+            if (mlds) store_mask(st0, c, rm);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         // Loop body for tile `it` computed from `stage` while tile it+1 is
         // staged into `nstage`; unrolled by two below so that both stage
         // addresses are compile-time LDS offsets.
-        auto body = [&](int it, char* stage, char* nstage) {
+        auto body = [&](int it, char* __restrict__ stage, char* __restrict__ nstage) {
             const bool more = it + 1 < c.t1;
-            if (more) load_tile(p, c, it + 1, with_v, rk, rv);
+            if (more) dma_tile(c, it + 1, with_v, nstage, wave);
             if (mlds && more) load_mask(p, c, it + 1, rm);
             const int j0 = it * C::BN;
             if (c.wave_rows && j0 < c.wave_kv_end) {
@@ -624,20 +622,21 @@ struct Prefill {
                     }
                 }
             }
-            if (more) store_tile(nstage, with_v, rk, rv);
             if (mlds && more) store_mask(nstage, c, rm);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's part of tile it+1 landed
             __syncthreads();
         };
         int it = c.t0;
         for (; it + 1 < c.t1; it += 2) {
-            body(it, smem, smem + SSTAGE);
-            body(it + 1, smem + SSTAGE, smem);
+            body(it, st0, st1);
+            body(it + 1, st1, st0);
         }
-        if (it < c.t1) body(it, smem, smem + SSTAGE);
+        if (it < c.t1) body(it, st0, st1);
     }
 
     template <int MODE>
-    __device__ __forceinline__ static void run(const AttnParams& p, char* smem) {
+    __device__ __forceinline__ static void run(const AttnParams& p, char* __restrict__ st0,
+                                               char* __restrict__ st1) {
         __shared__ int s_map[2];
         const int tid = threadIdx.x, lane = tid & 63;
         // wave index in a scalar register: everything derived from it is
@@ -691,11 +690,22 @@ struct Prefill {
         c.ktile = (uint32_t)((int64_t)C::BN * p.k.sn * C::ES);
         c.vtile = (uint32_t)((int64_t)C::BN * p.v.sn * C::ES);
         {
-            const int ch = tid % C::CHUNKS, kg = tid / C::CHUNKS;
+            // source of the 16 LDS bytes this lane writes in each copy
+            // instruction: K rows are padded (positions in the pad read as
+            // zeros), V rows are swizzled (position -> logical 16-byte unit)
 #pragma unroll
-            for (int kk = 0; kk < C::KPT; ++kk) {
-                c.koff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.k.sn + ch * 8) * C::ES);
-                c.voff[kk] = (uint32_t)(((int64_t)(kg * C::KPT + kk) * p.v.sn + ch * 8) * C::ES);
+            for (int k = 0; k < C::KMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                const int row = pos / C::KROW, byte = pos % C::KROW;
+                c.koff[k] = byte < D * C::ES
+                                ? (uint32_t)((int64_t)row * p.k.sn * C::ES + byte)
+                                : 0xFFFFFFF0u;
+            }
+#pragma unroll
+            for (int k = 0; k < C::VMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                const int row = pos / C::VROW, unit = (pos % C::VROW) / 16;
+                c.voff[k] = (uint32_t)((int64_t)row * p.v.sn * C::ES + ((unit ^ v_swz<C>(row)) << 4));
             }
         }
         c.mrow = nullptr;
@@ -775,16 +785,16 @@ struct Prefill {
 
         if constexpr (MODE == MODE_NONE) {
             const float inv = p.qdq ? 1.f / p.qscale : 1.f;
-            sweep<PASS_NONE>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            sweep<PASS_NONE>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o);
             if (p.qdq) factor *= p.qscale;
         } else if constexpr (MODE == MODE_SOFTMAX_QDQ || MODE == MODE_SOFTMAX_QDQ_NS) {
-            sweep<PASS_STATS>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            sweep<PASS_STATS>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o);
             const float l_tot = halves_sum(l_run);
             const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
-            sweep<PASS_FIXED, MODE == MODE_SOFTMAX_QDQ>(p, c, smem, qreg, sc, ac, m_run, l_run, inv, o);
+            sweep<PASS_FIXED, MODE == MODE_SOFTMAX_QDQ>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o);
             factor *= p.qscale;
         } else {
-            sweep<PASS_ONLINE>(p, c, smem, qreg, sc, ac, m_run, l_run, 0.f, o);
+            sweep<PASS_ONLINE>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o);
             const float l_tot = halves_sum(l_run);
             if (p.n_splits > 1) {
                 // split-KV: unnormalized O with its reference max and sum
@@ -832,8 +842,12 @@ struct Prefill {
 
 template <typename TI, int D, int MODE, int MK>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) char smem[2 * Prefill<TI, D, MK>::SSTAGE];
-    Prefill<TI, D, MK>::template run<MODE>(p, smem);
+    // two separate stage arrays: the compiler then knows that the copy into
+    // one stage never aliases the reads of the other, and does not wait for
+    // the copy before computing on the current stage
+    __shared__ __attribute__((aligned(16))) char st0[Prefill<TI, D, MK>::SSTAGE];
+    __shared__ __attribute__((aligned(16))) char st1[Prefill<TI, D, MK>::SSTAGE];
+    Prefill<TI, D, MK>::template run<MODE>(p, st0, st1);
 }
 
 // Split-KV combine: one workgroup per (row tile, query head) merges the

@@ -21,6 +21,17 @@ __device__ __forceinline__ int v_addr(int key, int d) {
     return key * C::VROW + (((byte >> 4) ^ v_swz<C>(key)) << 4) + (byte & 15);
 }
 
+// Buffer load of 16 bytes per lane written straight into LDS (no registers):
+// lane i's bytes land at lds + 16 i; a lane outside the descriptor's range
+// writes zeros.  Completion is tracked by vmcnt.  (The builtin exists only
+// for the device target; the host pass sees an empty body.)
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                             voff, 0, 0, 0);
+#endif
+}
+
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 // LDS transpose reads (gfx950): within each group of 16 lanes,
 // ds_read_b64_tr_b16 gives lane 4q+c the 16-bit element c of lanes 4k+q
