@@ -55,6 +55,7 @@ struct AttnParams {
     float* part_o;                    // [B, Hq, S, D]
     float* part_ml;                   // [B, Hq, S, 2]
     int32_t split_keys, n_splits;
+    int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs
 };
 
 // ---------------------------------------------------------------- lengths

@@ -302,6 +302,12 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     plan->grid_x = (int)gx;
     plan->grid_y = (int)(Hq / hw);
     if (plan->grid_y > 65535) return fail(GQA_ERR_UNSUPPORTED, "too many heads");
+    // MI355X has 8 XCDs (each with its own L2) that receive workgroup ids in
+    // turn; the prefill kernel remaps ids so that an XCD works through whole
+    // head groups when they divide evenly (GQA_ATTN_XCD_REMAP=0 turns it off).
+    p.xcds = plan->grid_y % 8 == 0 ? 8 : 0;
+    if (const char* e = std::getenv("GQA_ATTN_XCD_REMAP"))
+        if (std::atoi(e) == 0) p.xcds = 0;
     plan->kernel = K_PREFILL;
     plan->workspace = 0;
     p.n_splits = 1;
@@ -336,6 +342,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
             plan->workspace = (size_t)rows * Hq * S * (D + 2) * sizeof(float) + 256;
         }
     }
+    // the remap linearizes the grid in 32-bit arithmetic
+    if ((int64_t)plan->grid_x * plan->grid_y * p.n_splits > INT32_MAX) p.xcds = 0;
     return GQA_OK;
 }
 

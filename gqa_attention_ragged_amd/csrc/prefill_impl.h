@@ -14,10 +14,14 @@
 //   * blockIdx.x enumerates query-row tiles over the whole ragged batch
 //     (sum_b ceil(q_len_b / rows_per_wg)); the tile -> (b, tile) map is
 //     rebuilt on the device from the cumulative lengths, so the host never
-//     reads device memory.  blockIdx.y enumerates head groups.
-//   * The key loop streams 64-key tiles through double-buffered LDS: K
-//     row-major, V transposed (V^T[d][key]) so that both MFMA operands are
-//     read with 16-byte LDS loads.
+//     reads device memory.  blockIdx.y enumerates head groups, blockIdx.z
+//     key slices (split-KV).  When the head groups divide evenly over the
+//     XCDs, workgroup ids are remapped so that each XCD works through whole
+//     head groups (K/V cached in one L2).
+//   * The key loop streams 64-key tiles through double-buffered LDS, copied
+//     by buffer loads that write LDS directly: K row-major with padded rows,
+//     V row-major with XOR-swizzled 16-byte units, read as the BMM2 operand
+//     with the gfx950 LDS transpose loads.
 //   * Scores are computed transposed, S^T = K Q^T, with 32x32 MFMA tiles, so
 //     each lane owns one query row (lane % 32) and 16 of every 32 keys; the
 //     row max / sum need one exchange with lane ^ 32 only.  O is likewise
@@ -647,7 +651,22 @@ struct Prefill {
         // Tiles are enumerated sequence by sequence, row tile by row tile; the
         // workgroups take them in reverse so that, under causal masking, the
         // heaviest (last) row tiles of each sequence are dispatched first.
-        const int tile = gridDim.x - 1 - blockIdx.x;
+        int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+        if (p.xcds > 1) {
+            // Consecutive workgroup ids go to the XCDs in turn (id % xcds),
+            // each with its own L2.  Remapped, XCD x takes one contiguous
+            // block of the work items ordered (head group, split, row tile),
+            // so the K/V rows of a head group are fetched into one L2 rather
+            // than into all of them.
+            const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z, X = p.xcds;
+            const int n = nx * ny * nz, L = bx + nx * (by + ny * bz);
+            const int xcd = L % X, k = L / X, q = n / X, r = n % X;
+            const int li = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + k;
+            bx = li % nx;
+            bz = (li / nx) % nz;
+            by = li / (nx * nz);
+        }
+        const int tile = gridDim.x - 1 - bx;
 
         map_tile(p, tile, R, s_map);
         // (b, row tile) are workgroup-uniform: read them into scalar registers
@@ -664,8 +683,8 @@ struct Prefill {
         c.causal = p.causal != 0;
         const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
         const int hw = p.heads_per_wg;
-        const int h = blockIdx.y * hw + (wave % hw);
-        const int kvh = (blockIdx.y * hw) / p.group;
+        const int h = by * hw + (wave % hw);
+        const int kvh = (by * hw) / p.group;
         c.wr0 = row0 + (wave / hw) * 32;
         c.i = c.wr0 + lr;
         c.wave_rows = c.wr0 < c.q_len;
@@ -677,7 +696,7 @@ struct Prefill {
         c.t1 = (kv_end + C::BN - 1) / C::BN;
         if (p.n_splits > 1) {  // split-KV: this workgroup takes one slice of the keys
             const int per = p.split_keys / C::BN;
-            c.t0 = min((int)blockIdx.z * per, c.t1);
+            c.t0 = min(bz * per, c.t1);
             c.t1 = min(c.t0 + per, c.t1);
         }
         const int wave_last = min(c.wr0 + 32, c.q_len) - 1;
@@ -801,7 +820,7 @@ struct Prefill {
                 // (exp2 domain); the combine kernel merges the slices.
                 if (c.i < c.q_len) {
                     const int64_t row = (p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q) + c.i;
-                    const int64_t slot = (row * p.hq + h) * p.n_splits + blockIdx.z;
+                    const int64_t slot = (row * p.hq + h) * p.n_splits + bz;
                     float* po = p.part_o + slot * D;
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db)
