@@ -648,9 +648,6 @@ struct Prefill {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lr = lane & 31, lg = lane >> 5;
         const int R = p.rows_per_wg;
-        // Tiles are enumerated sequence by sequence, row tile by row tile; the
-        // workgroups take them in reverse so that, under causal masking, the
-        // heaviest (last) row tiles of each sequence are dispatched first.
         int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
         if (p.xcds > 1) {
             // Consecutive workgroup ids go to the XCDs in turn (id % xcds),
@@ -666,9 +663,8 @@ struct Prefill {
             bz = (li / nx) % nz;
             by = li / (nx * nz);
         }
-        const int tile = gridDim.x - 1 - bx;
-
-        map_tile(p, tile, R, s_map);
+        // dispatch position -> (sequence, row tile), heaviest first
+        map_tile(p, bx, R, s_map);
         // (b, row tile) are workgroup-uniform: read them into scalar registers
         // so that every address and buffer descriptor built from them is
         // scalar too (a descriptor in vector registers needs a loop per load).

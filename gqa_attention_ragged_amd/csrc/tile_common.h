@@ -48,33 +48,58 @@ __device__ __forceinline__ u32x2 tr8(const char* p) {
 }
 
 // ------------------------------------------------------------------ tile map
-// Row tile `tile` of the ragged batch -> (b, row tile within b), with the
-// tiles enumerated sequence by sequence (ceil(q_len_b / R) tiles each).
-// Wave 0 scans the per-sequence tile counts 64 sequences at a time; the
-// result lands in s_map[0..1] (b = -1 past the last tile).  Block-wide
-// barrier included.
-__device__ __forceinline__ void map_tile(const AttnParams& p, int tile, int R, int* s_map) {
+// Dispatch position `pos` -> (b, row tile within b); sequence b has
+// ceil(q_len_b / R) row tiles.  Positions run over the sequences by
+// decreasing KV length (ties: lower index first; more than 64 sequences:
+// index order), and within a sequence from its last row tile to its first,
+// so the heaviest work items (long rows of long sequences under causal
+// masking) start first and the lightest ones fill the tail.  Wave 0
+// computes the map; the result lands in s_map[0..1] (b = -1 past the last
+// tile).  Block-wide barrier included.
+__device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, int* s_map) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (wave == 0) {
         if (lane == 0) s_map[0] = -1;
-        int acc = 0;
-        for (int base = 0; base < p.batch; base += 64) {
-            const int b = base + lane;
-            int n = 0;
-            if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
-            int incl = n;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
+        if (p.batch <= 64) {
+            const int b = lane;
+            const int n = b < p.batch ? (q_len_of(p, b) + R - 1) / R : 0;
+            const int key = b < p.batch ? kv_len_of(p, b) : -1;
+            // rank of b in the dispatch order, then the row tiles ahead of it
+            int rank = 0;
+            for (int j = 0; j < p.batch; ++j) {
+                const int kj = __builtin_amdgcn_readlane(key, j);
+                rank += (kj > key) || (kj == key && j < b);
             }
-            const int excl = incl - n;
-            if (n > 0 && tile >= acc + excl && tile < acc + incl) {
+            int ahead = 0;
+            for (int j = 0; j < p.batch; ++j) {
+                const int nj = __builtin_amdgcn_readlane(n, j);
+                const int rj = __builtin_amdgcn_readlane(rank, j);
+                ahead += rj < rank ? nj : 0;
+            }
+            if (n > 0 && pos >= ahead && pos < ahead + n) {
                 s_map[0] = b;
-                s_map[1] = tile - acc - excl;
+                s_map[1] = n - 1 - (pos - ahead);
             }
-            acc += __shfl(incl, 63);
-            if (acc > tile) break;
+        } else {
+            int acc = 0;
+            for (int base = 0; base < p.batch; base += 64) {
+                const int b = base + lane;
+                int n = 0;
+                if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
+                int incl = n;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off);
+                    if (lane >= off) incl += y;
+                }
+                const int excl = incl - n;
+                if (n > 0 && pos >= acc + excl && pos < acc + incl) {
+                    s_map[0] = b;
+                    s_map[1] = n - 1 - (pos - acc - excl);
+                }
+                acc += __shfl(incl, 63);
+                if (acc > pos) break;
+            }
         }
     }
     __syncthreads();
