@@ -160,6 +160,11 @@ struct Prefill {
     typedef typename Vec8<T16>::type V8;
     // Bytes per pipeline stage: K tile, V tile and (mask kernels) a mask tile.
     static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? C::MBYTES : 0);
+    // When a tile's copy instructions do not divide evenly over the 4 waves,
+    // the waves without a last instruction still issue one (every lane out
+    // of range: zeros, no memory access) into a spare 1 KiB after the stage,
+    // so that the copy has no wave-dependent branches.
+    static constexpr int SPARE = (C::NKD % 4 || C::NVD % 4) ? 1024 : 0;
     // BMM1 B operand held in registers for the whole kernel: 8 x 16-bit
     // values per k-step, or 32 E4M3FN codes per k-step.
     typedef typename std::conditional<C::FP8, i32x8, V8>::type QOp;
@@ -266,16 +271,16 @@ struct Prefill {
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) {
             const int j = wave + 4 * k;
-            if (j < C::NKD)
-                buf_load_lds16(kr, stage + j * 1024, c.koff[k]);
+            const int dst = 4 * (k + 1) <= C::NKD || j < C::NKD ? j * 1024 : SSTAGE;
+            buf_load_lds16(kr, stage + dst, c.koff[k]);
         }
         if (!with_v) return;
         const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
 #pragma unroll
         for (int k = 0; k < C::VMAX; ++k) {
             const int j = wave + 4 * k;
-            if (j < C::NVD)
-                buf_load_lds16(vr, stage + C::KBYTES + j * 1024, c.voff[k]);
+            const int dst = 4 * (k + 1) <= C::NVD || j < C::NVD ? C::KBYTES + j * 1024 : SSTAGE;
+            buf_load_lds16(vr, stage + dst, c.voff[k]);
         }
     }
 
@@ -486,19 +491,26 @@ struct Prefill {
     // SAT: the quantized scores may exceed the format's range and are
     // saturated; without it the caller guarantees x = P / qscale stays below
     // the rounding limit (P <= 1), and the clamp is left out.
-    template <int KIND, bool SAT = true>
+    // PRIMED: the copy of the first tile into st0 was started by the caller
+    // (with the mask tile's registers in rm0).
+    template <int KIND, bool SAT = true, bool PRIMED = false>
     __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c,
                                                  char* __restrict__ st0, char* __restrict__ st1,
                                                  const QRegs& qreg, float sc, float ac,
-                                                 float& m_run, float& l_run, float inv, ORegs& o) {
+                                                 float& m_run, float& l_run, float inv, ORegs& o,
+                                                 const u32x4& rm0 = u32x4{}) {
         const bool with_v = KIND != PASS_STATS;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         u32x4 rm = {};
         const bool mlds = STAGED;
         if (c.t0 < c.t1) {
-            dma_tile(c, c.t0, with_v, st0, wave);
-            if (mlds) load_mask(p, c, c.t0, rm);
-            if (mlds) store_mask(st0, c, rm);
+            if constexpr (PRIMED) {
+                if (mlds) store_mask(st0, c, rm0);
+            } else {
+                dma_tile(c, c.t0, with_v, st0, wave);
+                if (mlds) load_mask(p, c, c.t0, rm);
+                if (mlds) store_mask(st0, c, rm);
+            }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
@@ -712,7 +724,7 @@ struct Prefill {
             for (int k = 0; k < C::KMAX; ++k) {
                 const int pos = (wave + 4 * k) * 1024 + lane * 16;
                 const int row = pos / C::KROW, byte = pos % C::KROW;
-                c.koff[k] = byte < D * C::ES
+                c.koff[k] = pos < C::KBYTES && byte < D * C::ES
                                 ? (uint32_t)((int64_t)row * p.k.sn * C::ES + byte)
                                 : 0xFFFFFFF0u;
             }
@@ -720,7 +732,9 @@ struct Prefill {
             for (int k = 0; k < C::VMAX; ++k) {
                 const int pos = (wave + 4 * k) * 1024 + lane * 16;
                 const int row = pos / C::VROW, unit = (pos % C::VROW) / 16;
-                c.voff[k] = (uint32_t)((int64_t)row * p.v.sn * C::ES + ((unit ^ v_swz<C>(row)) << 4));
+                c.voff[k] = pos < C::VBYTES
+                                ? (uint32_t)((int64_t)row * p.v.sn * C::ES + ((unit ^ v_swz<C>(row)) << 4))
+                                : 0xFFFFFFF0u;
             }
         }
         c.mrow = nullptr;
@@ -758,6 +772,15 @@ struct Prefill {
                      ((int64_t)b * p.m_sb + (int64_t)h * p.m_sh + (int64_t)c.i * p.m_si) * mes;
         }
 
+        // The copy of the first key tile (and its mask tile) starts before the
+        // Q loads, so that the two latencies overlap.
+        constexpr bool kFirstWithV = MODE != MODE_SOFTMAX_QDQ && MODE != MODE_SOFTMAX_QDQ_NS;
+        u32x4 rm0 = {};
+        if (c.t0 < c.t1) {
+            dma_tile(c, c.t0, kFirstWithV, st0, wave);
+            if constexpr (STAGED) load_mask(p, c, c.t0, rm0);
+        }
+
         // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg)
         QRegs qreg;
         {
@@ -783,9 +806,10 @@ struct Prefill {
                     qreg[ks] = a;
                 }
             }
-            // Q must be resident before the key loop: otherwise the compiler
-            // cannot tell the Q loads from the K/V prefetch of the loop and
-            // waits for every outstanding load before the first MFMA.
+            // Q (and the first tile) must be resident before the key loop:
+            // otherwise the compiler cannot tell the Q loads from the tile
+            // copies of the loop and waits for all of them before the first
+            // MFMA.
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
 
@@ -800,16 +824,16 @@ struct Prefill {
 
         if constexpr (MODE == MODE_NONE) {
             const float inv = p.qdq ? 1.f / p.qscale : 1.f;
-            sweep<PASS_NONE>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o);
+            sweep<PASS_NONE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o, rm0);
             if (p.qdq) factor *= p.qscale;
         } else if constexpr (MODE == MODE_SOFTMAX_QDQ || MODE == MODE_SOFTMAX_QDQ_NS) {
-            sweep<PASS_STATS>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o);
+            sweep<PASS_STATS, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
             const float l_tot = halves_sum(l_run);
             const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
             sweep<PASS_FIXED, MODE == MODE_SOFTMAX_QDQ>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o);
             factor *= p.qscale;
         } else {
-            sweep<PASS_ONLINE>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o);
+            sweep<PASS_ONLINE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
             const float l_tot = halves_sum(l_run);
             if (p.n_splits > 1) {
                 // split-KV: unnormalized O with its reference max and sum
@@ -860,8 +884,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
     // two separate stage arrays: the compiler then knows that the copy into
     // one stage never aliases the reads of the other, and does not wait for
     // the copy before computing on the current stage
-    __shared__ __attribute__((aligned(16))) char st0[Prefill<TI, D, MK>::SSTAGE];
-    __shared__ __attribute__((aligned(16))) char st1[Prefill<TI, D, MK>::SSTAGE];
+    typedef Prefill<TI, D, MK> P;
+    __shared__ __attribute__((aligned(16))) char st0[P::SSTAGE + P::SPARE];
+    __shared__ __attribute__((aligned(16))) char st1[P::SSTAGE + P::SPARE];
     Prefill<TI, D, MK>::template run<MODE>(p, st0, st1);
 }
 
