@@ -52,6 +52,7 @@ class Case:
     kv_lens: np.ndarray                     # per-batch valid KV lengths
     out_dtype: torch.dtype
     meta: dict = field(default_factory=dict)
+    tree_parents: Optional[torch.Tensor] = None  # int32, token-aligned with Q's rows, or None
 
     def kwargs(self) -> dict:
         """Operator arguments shared by the GPU binding and the oracle."""
@@ -60,13 +61,13 @@ class Case:
             query_form=self.query_form, kv_form=self.kv_form, causal_kind=self.causal_kind,
             norm=self.norm, qdq=self.qdq, qscale=self.qscale, scale=self.scale,
             k_descale=self.k_descale, v_descale=self.v_descale, num_heads=self.num_heads,
-            kv_num_heads=self.kv_num_heads,
+            kv_num_heads=self.kv_num_heads, tree_parents=self.tree_parents,
         )
 
     def to_host(self) -> "Case":
         """Same case with every tensor copied to host memory."""
         c = Case(**{k: getattr(self, k) for k in self.__dataclass_fields__})
-        for k in ("q", "k", "v", "mask", "query_lengths", "kv_lengths"):
+        for k in ("q", "k", "v", "mask", "query_lengths", "kv_lengths", "tree_parents"):
             t = getattr(self, k)
             if t is not None:
                 setattr(c, k, t.cpu())
@@ -112,7 +113,7 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
              causal_kind: str = "none", norm: str = "softmax", qdq: Optional[str] = None,
              qscale: float = 1.0, scale: Optional[float] = None, dist: str = "normal",
              kv_fp8_from: Optional[torch.dtype] = None, device="cpu", name="case",
-             nan_padding: bool = True) -> Case:
+             nan_padding: bool = True, tree: Optional[str] = None) -> Case:
     """Draw one operator instance.
 
     q_lens / kv_lens: per-sequence valid lengths (sequences of ints).
@@ -121,6 +122,8 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
     mask_kind: None, 'bool', or an additive dtype name 'f16' | 'bf16' | 'f32'.
     kv_fp8_from: draw K/V in this dtype, then store them as E4M3FN with a
       per-tensor fp32 descale s = amax / 448 (the stored code is x / s).
+    tree: draft-token parents for tree decoding, token-aligned with Q's rows
+      (see ``tree_parents``); None for ordinary attention.
     """
     kv_dtype = kv_dtype or dtype
     q_lens = np.asarray(q_lens, dtype=np.int64)
@@ -221,6 +224,16 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
                 s == 1 for s in full[:4 - mask_rank]) else mask
         mask = mask.to(device)
 
+    tree_parents = None
+    if tree is not None:
+        rows = int(q_lens.sum()) + q_slack if query_form == "packed_nhd" else B * n_q
+        par = np.full(rows, -1, dtype=np.int32)
+        for b in range(B):
+            L = int(q_lens[b])
+            row0 = int(ql_cum[b]) if query_form == "packed_nhd" else b * n_q
+            par[row0:row0 + L] = tree_parents_for(rng, L, tree)
+        tree_parents = torch.from_numpy(par).to(device)
+
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out_dtype = torch.float16 if dtype == FP8 else dtype
@@ -229,7 +242,41 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
                 causal_kind=causal_kind, norm=norm, qdq=qdq, qscale=float(qscale),
                 scale=float(scale), k_descale=float(k_descale), v_descale=float(v_descale),
                 num_heads=num_heads, kv_num_heads=kv_num_heads, q_lens=q_lens, kv_lens=kv_lens,
-                out_dtype=out_dtype, meta=dict(seed=seed))
+                out_dtype=out_dtype, meta=dict(seed=seed), tree_parents=tree_parents)
+
+
+def tree_parents_for(rng, n: int, kind: str) -> np.ndarray:
+    """Parents of n draft tokens in topological order (parent < child; -1 =
+    attached to the committed context).
+      chain:  t - 1 (a single path: the ordinary causal case);
+      star:   -1 for every token;
+      random: uniform in [-1, t - 1];
+      spec:   levels of growing width (1, 2, 4, 8, then 16 per level), each
+              token's parent drawn from the previous level -- the shape of a
+              speculative-decoding draft tree;
+      bad:    random, with some parents out of range (>= t or < -1)."""
+    t = np.arange(n)
+    if kind == "chain":
+        return (t - 1).astype(np.int32)
+    if kind == "star":
+        return np.full(n, -1, dtype=np.int32)
+    if kind in ("random", "bad"):
+        par = np.array([int(rng.integers(-1, i)) if i > 0 else -1 for i in range(n)], dtype=np.int32)
+        if kind == "bad" and n:
+            pick = rng.random(n) < 0.3
+            junk = rng.integers(-5, n + 5, size=n).astype(np.int32)
+            par = np.where(pick, junk, par).astype(np.int32)
+        return par
+    if kind == "spec":
+        par = np.full(n, -1, dtype=np.int32)
+        prev, start, width = [-1], 0, 1
+        while start < n:
+            level = list(range(start, min(n, start + width)))
+            for i in level:
+                par[i] = prev[int(rng.integers(0, len(prev)))]
+            prev, start, width = level, start + len(level), min(16, width * 2)
+        return par
+    raise ValueError(kind)
 
 
 def _to_fp8_per_tensor(x: torch.Tensor, form: str, lens) -> tuple[torch.Tensor, float]:

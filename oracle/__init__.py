@@ -70,6 +70,7 @@ class _Args(ctypes.Structure):
         ("num_heads", ctypes.c_int32),
         ("kv_num_heads", ctypes.c_int32),
         ("amb_rel", ctypes.c_double),
+        ("tree_parents", ctypes.c_void_p),
     ]
 
 
@@ -174,6 +175,7 @@ def _args(q, k, v, mask, query_lengths, kv_lengths, batch, query_form, kv_form, 
     a.num_heads = num_heads
     a.kv_num_heads = kv_num_heads
     a.amb_rel = amb_rel
+    a.tree_parents = None
     return a
 
 
@@ -194,11 +196,14 @@ def list_rows(q, k, v, *, query_lengths=None, kv_lengths=None, batch=None,
 def attention(q, k, v, mask=None, *, query_lengths=None, kv_lengths=None, batch=None,
               query_form="padded_bhnd", kv_form="padded_bhnd", causal_kind="none",
               norm="softmax", qdq=None, qscale=1.0, scale=1.0, k_descale=1.0, v_descale=1.0,
-              num_heads=None, kv_num_heads=None, rows=None, amb_rel=1e-5) -> OracleResult:
+              num_heads=None, kv_num_heads=None, rows=None, amb_rel=1e-5,
+              tree_parents=None) -> OracleResult:
     """Evaluate the operator on host tensors (raw storage dtypes).
 
     ``rows`` selects output rows (b, h, i); default is every valid row.
     ``num_heads`` / ``kv_num_heads`` default to Q's / K's head dimension.
+    ``tree_parents``: int32 parent index of each query row's draft token
+    (token-aligned with Q's rows: [T_q] packed, [B, N_q] padded), or None.
     """
     if num_heads is None:
         num_heads = q.shape[1]
@@ -208,6 +213,10 @@ def attention(q, k, v, mask=None, *, query_lengths=None, kv_lengths=None, batch=
     a = _args(q, k, v, mask, query_lengths, kv_lengths, batch, query_form, kv_form, causal_kind,
               norm, qdq, qscale, scale, k_descale, v_descale, num_heads, kv_num_heads, amb_rel,
               keep)
+    if tree_parents is not None:
+        tp = torch.as_tensor(tree_parents).to("cpu", torch.int32).contiguous()
+        keep.append(tp)
+        a.tree_parents = tp.data_ptr()
     lib = _load()
     if rows is None:
         n = lib.oracle_count_rows(ctypes.byref(a))

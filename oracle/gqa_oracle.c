@@ -40,6 +40,16 @@
  *     to +-448, int8 to [-128, 127]), dequantizes by multiplying back, and
  *     is applied to the normalized P (final max and sum); no renormalization.
  *
+ * Tree decoding (TensorRT Edge-LLM "TensorRT Plugins Guide", AttentionPlugin:
+ * tree decoding attention for speculative decoding, with tree parent data
+ * carried row by row alongside the query rows).  When tree parents are
+ * given, the q_len_b query rows of sequence b are draft tokens whose keys
+ * are the last q_len_b valid keys (draft t at key kv_len_b - q_len_b + t);
+ * parent[t] in [0, t-1] names the draft it extends, any other value hangs
+ * it off the committed context.  Row i may attend every context key
+ * (j < kv_len_b - q_len_b) and the drafts on its own ancestor chain, itself
+ * included; this rule is ANDed with the causal kind and the mask.
+ *
  * Alongside O the oracle returns, per output element, the largest change a
  * different rounding of "ambiguous" quantization inputs could make
  * (|x - nearest rounding midpoint| <= amb_rel * |x|), so that a GPU result
@@ -75,6 +85,7 @@ typedef struct {
     float scale, qscale, k_descale, v_descale;
     int32_t num_heads, kv_num_heads;
     double amb_rel;
+    const int32_t* tree_parents; /* [T_q] (packed Q) or [B, N_q] (padded Q), or NULL */
 } or_args;
 
 /* ---- exact decoding of the storage formats -------------------------- */
@@ -200,6 +211,22 @@ static int64_t mask_off(const or_tensor* m, int b, int h, int64_t i, int64_t j) 
     return off;
 }
 
+/* Tree rule: may row i of sequence b attend key j?  Walks the parent chain
+ * from draft i to the context; a parent outside [0, u-1] ends the chain. */
+static int tree_allows(const or_args* a, int b, int64_t i, int64_t j, int64_t ql, int64_t kl) {
+    const int64_t base = kl - ql;
+    if (j < base) return 1;
+    const int64_t t = j - base;
+    const int64_t row0 = a->query_form == OR_PACKED ? (int64_t)a->query_lengths[b]
+                                                     : (int64_t)b * a->q.shape[2];
+    for (int64_t u = i; u >= 0;) {
+        if (u == t) return 1;
+        const int32_t par = a->tree_parents[row0 + u];
+        u = (par >= 0 && par < u) ? (int64_t)par : -1;
+    }
+    return 0;
+}
+
 /* Host-side guard: every row the definition reads lies inside its tensor. */
 static int rows_in_bounds(const or_args* a, int b, int64_t ql, int64_t kl) {
     if (ql < 0 || kl < 0) return 0;
@@ -284,6 +311,7 @@ int oracle_rows(const or_args* a, const int32_t* rows, int64_t nrows, double* ou
             int allowed = 1;
             if (a->causal_kind == OR_CAUSAL_UPPER_LEFT) allowed = (j <= i);
             else if (a->causal_kind == OR_CAUSAL_LOWER_RIGHT) allowed = (j <= i + (kl - ql));
+            if (a->tree_parents) allowed = allowed && tree_allows(a, b, i, j, ql, kl);
             double add = 0.0;
             if (has_mask) {
                 double mv = load_elem(&a->mask, mask_off(&a->mask, b, h, i, j));

@@ -21,6 +21,32 @@ def _f64(t: torch.Tensor) -> np.ndarray:
     return t.double().numpy()
 
 
+def _tree_allowed(case, b: int, L: int, kv: int, nq: int, nk: int) -> np.ndarray:
+    """[nq, nk] bool: the tree-decoding rule for sequence b (TensorRT
+    Edge-LLM "TensorRT Plugins Guide", AttentionPlugin, tree decoding).
+    Formulated as a reachability closure instead of a parent walk: E[u, p]
+    marks the edge draft u -> parent p (p in [0, u-1]); R = (I + E)^(L)
+    under boolean matrix products gives R[i, t] = t is draft i or one of its
+    ancestors.  Context keys (j < kv - L) are always allowed."""
+    tp = case.tree_parents.cpu().numpy().astype(np.int64)
+    row0 = int(np.sum(case.q_lens[:b])) if case.query_form == "packed_nhd" else b * case.q.shape[2]
+    par = tp[row0:row0 + L]
+    E = np.zeros((L, L), dtype=np.int64)
+    for u in range(L):
+        if 0 <= par[u] < u:
+            E[u, par[u]] = 1
+    R = np.eye(L, dtype=np.int64)
+    step = np.eye(L, dtype=np.int64) + E
+    for _ in range(max(L, 1)):
+        R = np.minimum(R @ step, 1)
+    out = np.ones((nq, nk), dtype=bool)
+    base = kv - L
+    for jj in range(max(base, 0), min(kv, nk)):
+        t = jj - base
+        out[:L, jj] = R[:, t].astype(bool)
+    return out
+
+
 def dense(case) -> tuple[np.ndarray, np.ndarray]:
     """(Y [B, Hq, Nq, D] float64, valid [B, Hq, Nq] bool) for a host Case."""
     B, Hq, Hkv = case.batch, case.num_heads, case.kv_num_heads
@@ -62,6 +88,8 @@ def dense(case) -> tuple[np.ndarray, np.ndarray]:
             a &= j <= i
         elif case.causal_kind == "lower_right":
             a &= j <= i + (kl[b] - ql[b])
+        if case.tree_parents is not None:
+            a &= _tree_allowed(case, b, int(ql[b]), int(kl[b]), nq, nk)
         allowed[b] = a
 
     if case.mask is not None:

@@ -65,8 +65,18 @@ def subcase(case, bs):
         kv_lengths = torch.from_numpy(np.concatenate([[0], np.cumsum(kl)]).astype(np.int32))
     elif c.kv_lengths is not None:
         kv_lengths = torch.from_numpy(kl.astype(np.int32))
+    tree = None
+    if c.tree_parents is not None:  # token-aligned with Q's rows
+        tp = c.tree_parents.cpu()
+        if c.query_form == "packed_nhd":
+            starts = np.concatenate([[0], np.cumsum(c.q_lens)])
+            tree = torch.cat([tp[int(starts[b]):int(starts[b] + c.q_lens[b])] for b in bs])
+        else:
+            n_q = c.q.shape[2]
+            tree = torch.cat([tp[b * n_q:(b + 1) * n_q] for b in bs])
     sub = synth.Case(**{f: getattr(c, f) for f in c.__dataclass_fields__})
     sub.q, sub.k, sub.v, sub.mask = q, k, v, mask
+    sub.tree_parents = tree
     sub.query_lengths, sub.kv_lengths = query_lengths, kv_lengths
     sub.batch = len(bs)
     sub.q_lens, sub.kv_lens = ql, kl
