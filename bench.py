@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # dense MFMA TFLOP/s
 HBM_PEAK = 8000.0  # GB/s
-WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "kvu", "1")
+WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "tree", "kvu", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
                 "gqa_attention_ragged_amd/csrc/prefill_impl.h",
@@ -68,6 +68,8 @@ def work_of(case) -> dict:
             case.batch * case.num_heads * D * (q_b + 2)
         return {"kind": "decode", "bytes": byts}
     pairs = 0
+    tree = None if case.tree_parents is None else case.tree_parents.cpu().numpy()
+    starts = np.concatenate([[0], np.cumsum(ql)])
     for b in range(case.batch):
         i = np.arange(ql[b])
         if case.causal_kind == "none":
@@ -75,6 +77,18 @@ def work_of(case) -> dict:
         else:
             diag = 0 if case.causal_kind == "upper_left" else kl[b] - ql[b]
             n = np.clip(i + diag + 1, 0, kl[b])
+        if tree is not None:
+            # tree decoding (causal none): the context plus the draft's own
+            # ancestor chain, itself included
+            row0 = int(starts[b]) if case.query_form == "packed_nhd" else b * case.q.shape[2]
+            par = tree[row0:row0 + ql[b]]
+            depth = np.zeros(ql[b], dtype=np.int64)
+            for t in range(int(ql[b])):
+                u, d = t, 0
+                while 0 <= par[u] < u:
+                    u, d = int(par[u]), d + 1
+                depth[t] = d
+            n = np.minimum(n, kl[b] - ql[b] + depth + 1)
         pairs += int(n.sum())
     pairs *= case.num_heads
     return {"kind": "prefill", "flop": 4 * D * pairs, "pairs": pairs}

@@ -63,6 +63,7 @@ class GqaArgs(ctypes.Structure):
         ("v_descale", ctypes.c_float),
         ("num_heads", ctypes.c_int32),
         ("kv_num_heads", ctypes.c_int32),
+        ("tree_parents", ctypes.c_void_p),
     ]
 
 
@@ -149,13 +150,14 @@ def tensor_view(t: Optional[torch.Tensor]) -> GqaTensor:
 def make_args(q, k, v, attn_mask=None, out=None, *, query_lengths=None, kv_lengths=None,
               batch=None, query_form="padded_bhnd", kv_form="padded_bhnd", causal_kind="none",
               norm="softmax", qdq=None, qscale=1.0, scale=1.0, k_descale=1.0, v_descale=1.0,
-              num_heads=None, kv_num_heads=None) -> GqaArgs:
+              num_heads=None, kv_num_heads=None, tree_parents=None) -> GqaArgs:
     """Fill a gqa_attn_args_t from tensors (no copies, no checks)."""
     a = GqaArgs()
     a.q, a.k, a.v = tensor_view(q), tensor_view(k), tensor_view(v)
     a.attn_mask = tensor_view(attn_mask)
     a.out = tensor_view(out)
-    for name, t in (("query_lengths", query_lengths), ("kv_lengths", kv_lengths)):
+    for name, t in (("query_lengths", query_lengths), ("kv_lengths", kv_lengths),
+                    ("tree_parents", tree_parents)):
         if t is not None and t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
         setattr(a, name, None if t is None else t.data_ptr())

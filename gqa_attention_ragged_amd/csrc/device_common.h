@@ -56,6 +56,7 @@ struct AttnParams {
     float* part_ml;                   // [B, Hq, S, 2]
     int32_t split_keys, n_splits;
     int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs
+    const int32_t* tree;              // draft-token parents, token-aligned with Q's rows, or null
 };
 
 // ---------------------------------------------------------------- lengths

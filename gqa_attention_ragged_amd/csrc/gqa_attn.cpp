@@ -189,6 +189,10 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
 
     // supported combinations
     if (D != 64 && D != 128) return fail(GQA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
+    // tree decoding: each wave resolves the ancestor chains of up to 64
+    // drafts per sequence (one lane per draft)
+    if (a->tree_parents && qf == GQA_FORM_PADDED_BHND && Nq > 64)
+        return fail(GQA_ERR_UNSUPPORTED, "tree_parents with padded Q needs N_q <= 64");
     if (qdt == GQA_DT_FP8_E4M3 && a->qdq != GQA_QDQ_FP8_E4M3)
         return fail(GQA_ERR_UNSUPPORTED, "fp8 Q/K/V needs fp8 Q/DQ of the scores");
     const int64_t G = Hq / Hkv;
@@ -226,6 +230,9 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     p.o_sn = ov.sn;
     p.ql = a->query_lengths;
     p.kl = a->kv_lengths;
+    // With one query row per sequence (the decode step) the row is its own
+    // only draft and the tree rule allows every key: the tree has no effect.
+    p.tree = a->tree_parents;
     p.q_packed = qf;
     p.kv_packed = kf;
     p.batch = (int)B;
@@ -288,9 +295,10 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // mask broadcasts over heads, is 1 or 2 bytes wide with contiguous keys
     // and 16-byte aligned rows whose key extent is a whole number of 16-byte
     // chunks (tiles are loaded in 16-byte chunks), and the workgroup covers
-    // 32 rows.
+    // 32 rows; with tree decoding a mask is read per lane (the generic
+    // variant carries the tree rule).
     p.mask_lds = 0;
-    if (m.data && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
+    if (m.data && !a->tree_parents && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
         (p.mask_kind == gqa::MASK_BOOL || p.mask_kind == gqa::MASK_F16 ||
          p.mask_kind == gqa::MASK_BF16)) {
         const int64_t es = p.mask_kind == gqa::MASK_BOOL ? 1 : 2;
@@ -505,6 +513,6 @@ const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_last_hip_error(void) { return g_hip_err; }
 
-int gqa_attn_abi_version(void) { return 2; }
+int gqa_attn_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -145,12 +145,15 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Mask variants of the general kernel: none; read per lane from global memory
 // (any kind and layout); staged through LDS as 16-bit additive values -- f16
-// (an f16 mask, or a bool mask converted to 0 / -inf while staging) or bf16.
-enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3 };
+// (an f16 mask, or a bool mask converted to 0 / -inf while staging) or bf16;
+// no mask but tree decoding.  The tree rule is compiled only into the
+// generic and tree variants (a tree with a mask takes the generic one).
+enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3, MK_TREE = 4 };
 
 template <typename TI, int D, int MK>
 struct Prefill {
-    static constexpr bool HAS_MASK = MK != MK_NONE;
+    static constexpr bool HAS_MASK = MK != MK_NONE && MK != MK_TREE;
+    static constexpr bool TREE = MK == MK_GENERIC || MK == MK_TREE;  // tree rule compiled in
     static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16;
     typedef Cfg<TI, D> C;
     // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
@@ -191,7 +194,17 @@ struct Prefill {
         int mrow_l, mchunk;   // staged mask: this thread's (row, 16-byte chunk); row < 0: idle
         bool mbool;           // staged mask: bool source (converted to f16 0 / -inf)
         int i;                // this lane's query row
+        bool tree;            // tree decoding: the last q_len keys are draft tokens
+        int tbase;            // key of draft 0 (kv_len - q_len)
+        uint32_t anc_lo, anc_hi;  // drafts on this row's ancestor chain (bit t = draft t)
     };
+
+    // Tree rule for draft t (key tbase + t) of this lane's row: the row's own
+    // draft and its ancestors (rows beyond the first 64 drafts: itself only).
+    __device__ __forceinline__ static bool tree_ok(const Ctx& c, int t) {
+        const uint32_t w = t < 32 ? c.anc_lo : c.anc_hi;
+        return t == c.i || (t < 64 && ((w >> (t & 31)) & 1u));
+    }
 
     // A buffer window starting at tile `tile`: the wave-uniform base moves
     // with the tile (scalar arithmetic only) and the range ends with the last
@@ -332,7 +345,8 @@ struct Prefill {
     __device__ __forceinline__ static bool cl_full(const AttnParams& p, const Ctx& c, int tile) {
         const int j0 = tile * C::BN;
         return j0 + C::BN <= c.kv_len && c.wr0 + 32 <= c.q_len &&
-               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag);
+               !(p.causal && j0 + C::BN - 1 > c.wr0 + c.diag) &&
+               !(TREE && c.tree && j0 + C::BN > c.tbase);
     }
 
     // Mask-free kernels: mark the keys a row may not see with -inf and keep
@@ -343,6 +357,18 @@ struct Prefill {
         int lim = c.i < c.q_len ? c.kv_len : 0;
         if (c.causal) lim = min(lim, c.i + c.diag + 1);
         const int rel = lim - (tile * C::BN + lg * 4);  // key offset limit for this lane
+        if (TREE && c.tree) {
+            const int t0 = tile * C::BN + lg * 4 - c.tbase;  // draft index of offset 0
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int off = kb * 32 + (r >> 2) * 8 + (r & 3);
+                    const bool ok = off < rel && (t0 + off < 0 || tree_ok(c, t0 + off));
+                    s[kb][r] = ok ? s[kb][r] : -INFINITY;
+                }
+            return;
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -388,6 +414,7 @@ struct Prefill {
                     const int j = jg + u;
                     const int r = rq * 4 + u;
                     bool a = row_ok && j < c.kv_len && (p.causal == 0 || j <= c.i + c.diag);
+                    if (TREE && c.tree && j >= c.tbase) a = a && tree_ok(c, j - c.tbase);
                     float v = s[kb][r] * sc;
                     if (MK == MK_GENERIC && p.mask_kind == MASK_BOOL) {
                         a = a && mg.ok[u];
@@ -689,6 +716,9 @@ struct Prefill {
         c.kv_len = kv_len_of(p, b);
         c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
         c.causal = p.causal != 0;
+        c.tree = TREE && p.tree != nullptr;
+        c.tbase = c.kv_len - c.q_len;
+        c.anc_lo = c.anc_hi = 0u;
         const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
         const int hw = p.heads_per_wg;
         const int h = by * hw + (wave % hw);
@@ -696,6 +726,34 @@ struct Prefill {
         c.wr0 = row0 + (wave / hw) * 32;
         c.i = c.wr0 + lr;
         c.wave_rows = c.wr0 < c.q_len;
+        if (TREE && c.tree) {
+            // Ancestor sets of the sequence's first 64 drafts by pointer
+            // jumping, lane l = draft l: A_l starts as {l} and J_l as its
+            // parent; each round A_l |= A_{J_l}, J_l = J_{J_l} doubles the
+            // chain length covered, so 6 rounds cover any chain of 64.
+            const int64_t prow = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
+            int par = lane < c.q_len ? p.tree[prow + lane] : -1;
+            int jmp = (par >= 0 && par < lane) ? par : -1;
+            uint32_t a_lo = lane < c.q_len && lane < 32 ? 1u << lane : 0u;
+            uint32_t a_hi = lane < c.q_len && lane >= 32 ? 1u << (lane - 32) : 0u;
+#pragma unroll
+            for (int round = 0; round < 6; ++round) {
+                const int src = jmp >= 0 ? jmp : lane;
+                const uint32_t o_lo = __shfl(a_lo, src), o_hi = __shfl(a_hi, src);
+                const int o_j = __shfl(jmp, src);
+                if (jmp >= 0) {
+                    a_lo |= o_lo;
+                    a_hi |= o_hi;
+                    jmp = o_j;
+                }
+            }
+            const int mine = c.i & 63;
+            const uint32_t m_lo = __shfl(a_lo, mine), m_hi = __shfl(a_hi, mine);
+            if (c.i < 64) {
+                c.anc_lo = m_lo;
+                c.anc_hi = m_hi;
+            }
+        }
         const int wg_last = min(row0 + R, c.q_len) - 1;
         int kv_end = c.kv_len;
         if (p.causal) kv_end = min(kv_end, wg_last + c.diag + 1);
@@ -941,7 +999,9 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
 template <typename TI, int D, int MODE>
 static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
-    if (p.mask_kind == MASK_NONE)
+    if (p.mask_kind == MASK_NONE && p.tree)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_TREE>), grid, dim3(256), 0, stream, p);
+    else if (p.mask_kind == MASK_NONE)
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_NONE>), grid, dim3(256), 0, stream, p);
     else if (!p.mask_lds)
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_GENERIC>), grid, dim3(256), 0, stream, p);

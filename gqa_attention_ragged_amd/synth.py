@@ -310,7 +310,7 @@ def _to_fp8_per_tensor(x: torch.Tensor, form: str, lens) -> tuple[torch.Tensor, 
 # The five workload configurations (LLM-shaped prefill, chunked context,
 # decode and quantized attention), at their full sizes.
 # --------------------------------------------------------------------------
-CONFIGS = ("1", "2", "3", "4a", "4b", "5a", "5b")
+CONFIGS = ("1", "2", "3", "4a", "4b", "5a", "5b", "tree")
 
 DESCRIPTIONS = {
     "1": "tiny padded MHA fp16 B=2 H=4 N=128 D=64",
@@ -320,12 +320,14 @@ DESCRIPTIONS = {
     "4b": "decode fp8 e4m3 KV (per-tensor fp32 descale) B=128 Nkv=32768 Hq=32 Hkv=8 D=128",
     "5a": "quantized attention fp8 Q/K/V B=4 N=4096 Hq=32 Hkv=8 D=128 causal, P fp8 Q/DQ 1/448",
     "5b": "quantized attention as 5a plus bool mask [4,1,4096,4096] 90% true",
+    "tree": ("tree (speculative) decoding fp16 B=32, 64 draft tokens per sequence in a "
+             "1-2-4-8-16-wide tree, context U[1024,8192], Hq=32 Hkv=8 D=128"),
 }
 
 
 def config_lengths(cfg: str):
     """(q_lens, kv_lens) of a configuration (drawn first from its seed)."""
-    seed = {"1": 1, "2": 2, "3": 3, "4a": 4, "4b": 4, "5a": 5, "5b": 5}[cfg]
+    seed = {"1": 1, "2": 2, "3": 3, "4a": 4, "4b": 4, "5a": 5, "5b": 5, "tree": 6}[cfg]
     rng = np.random.Generator(np.random.PCG64(seed))
     if cfg == "1":
         return np.full(2, 128), np.full(2, 128)
@@ -339,6 +341,9 @@ def config_lengths(cfg: str):
     if cfg in ("4a", "4b"):
         kv = rng.integers(512, 32769, size=128)
         return np.ones(128, dtype=np.int64), kv
+    if cfg == "tree":
+        ctx = rng.integers(1024, 8193, size=32)
+        return np.full(32, 64), ctx + 64
     return np.full(4, 4096), np.full(4, 4096)
 
 
@@ -359,6 +364,11 @@ def make_config(cfg: str, device="cpu") -> Case:
                         head_dim=128, query_form="packed_nhd", kv_form="padded_bhnd", n_kv=8192,
                         dtype=torch.float16, causal_kind="lower_right", mask_kind="f16",
                         mask_p=0.1, mask_value=-10000.0, device=device, name="cfg3")
+    if cfg == "tree":
+        # the 64 drafts' keys are the last 64 valid KV rows of each sequence
+        return generate(seed=6, q_lens=q_lens, kv_lens=kv_lens, num_heads=32, kv_num_heads=8,
+                        head_dim=128, n_q=64, n_kv=8192 + 64, dtype=torch.float16,
+                        tree="spec", device=device, name="cfgtree")
     if cfg in ("4a", "4b"):
         return generate(seed=4, q_lens=q_lens, kv_lens=kv_lens, num_heads=32, kv_num_heads=8,
                         head_dim=128, n_q=1, n_kv=32768, dtype=torch.float16,

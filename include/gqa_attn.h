@@ -35,6 +35,17 @@
  *     beyond query_lengths[B]) are never written, and padding of Q/K/V is
  *     never read.
  *
+ * Tree decoding (TensorRT Edge-LLM "TensorRT Plugins Guide", AttentionPlugin:
+ * tree decoding attention, used by speculative decoding; tree parent data
+ * follows the query rows).  With tree_parents given, the q_len_b query rows
+ * of sequence b are draft tokens whose keys and values are the last q_len_b
+ * valid KV rows (draft t at key kv_len_b - q_len_b + t).  tree_parents
+ * holds, token-aligned with Q's rows, the parent draft of each token:
+ * parent[t] in [0, t-1], any other value attaches the token to the
+ * committed context.  Row i may attend every key j < kv_len_b - q_len_b and
+ * the drafts on its own ancestor chain, itself included; the rule is ANDed
+ * with causal_kind and the mask.
+ *
  * Ownership: the caller owns every buffer (all device pointers unless noted);
  * the library never allocates, frees or synchronizes on the forward path
  * and launches asynchronously on the caller's stream.
@@ -102,6 +113,11 @@ typedef struct {
  * batch: B.  Must equal q.shape[0] / k.shape[0] for padded forms; when both
  *      forms are packed it is the only source of B on the host.
  * out: Y in q's form and shape; dtype of q, except f16 when q is fp8.
+ * tree_parents: optional device int32, token-aligned with q's rows ([T_q]
+ *      packed, [B, N_q] contiguous padded); see "Tree decoding" above.
+ *      Padded q needs N_q <= 64.  Packed q: a sequence's drafts beyond the
+ *      first 64 attend the context and themselves only (device-side limit
+ *      of this build).
  *
  * Device-side length preconditions (not checked on the host, which never
  * reads device memory): lengths non-negative and monotone, query_lengths[0]
@@ -126,6 +142,7 @@ typedef struct {
     float v_descale;     /* 1.0f unless V is an fp8 cache */
     int32_t num_heads;    /* H_q */
     int32_t kv_num_heads; /* H_kv; H_q % H_kv == 0 */
+    const int32_t* tree_parents; /* NULL: no tree (ordinary attention) */
 } gqa_attn_args_t;
 
 /* Check every host-visible property of args; launches nothing, touches no
@@ -156,7 +173,7 @@ const char* gqa_attn_last_error(void);
 int gqa_attn_last_hip_error(void);
 
 /* Library ABI version (bumped on any change of these declarations or of
- * those in gqa_kv_cache.h; 2 adds the KV-cache update). */
+ * those in gqa_kv_cache.h; 2 adds the KV-cache update, 3 tree_parents). */
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

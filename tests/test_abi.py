@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "gqa_kv_cache_update" in names and "gqa_kv_cache_update_validate" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 2
+    assert lib.gqa_attn_abi_version() == 3
 
 
 _addr = [0x100000]
@@ -212,3 +212,18 @@ def test_kv_update_validate_rejects():
     assert capi.gqa_kv_cache_update_validate(a) == 1  # aliasing with other strides
     a = kv_args(dt=F32)
     assert capi.gqa_kv_cache_update_validate(a) == 1  # dtype
+
+
+def test_tree_parents_validation():
+    """Tree decoding resolves up to 64 drafts per sequence: padded Q with
+    N_q > 64 is rejected on the host; packed Q and N_q <= 64 pass."""
+    a = base_args(nq=64)
+    a.tree_parents = 0x7200000
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a = base_args(nq=65, nkv=80)
+    a.tree_parents = 0x7200000
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+    assert "tree_parents" in capi.last_error()
+    a = base_args(PACKED, PADDED, nq=100, nkv=120)
+    a.tree_parents = 0x7200000
+    assert st(a) == capi.GQA_OK, capi.last_error()
