@@ -53,6 +53,7 @@ class Case:
     out_dtype: torch.dtype
     meta: dict = field(default_factory=dict)
     tree_parents: Optional[torch.Tensor] = None  # int32, token-aligned with Q's rows, or None
+    kv_page_table: Optional[torch.Tensor] = None  # int32 [B, 2, max_pages] (kv_form "paged")
 
     def kwargs(self) -> dict:
         """Operator arguments shared by the GPU binding and the oracle."""
@@ -62,12 +63,14 @@ class Case:
             norm=self.norm, qdq=self.qdq, qscale=self.qscale, scale=self.scale,
             k_descale=self.k_descale, v_descale=self.v_descale, num_heads=self.num_heads,
             kv_num_heads=self.kv_num_heads, tree_parents=self.tree_parents,
+            kv_page_table=self.kv_page_table,
         )
 
     def to_host(self) -> "Case":
         """Same case with every tensor copied to host memory."""
         c = Case(**{k: getattr(self, k) for k in self.__dataclass_fields__})
-        for k in ("q", "k", "v", "mask", "query_lengths", "kv_lengths", "tree_parents"):
+        for k in ("q", "k", "v", "mask", "query_lengths", "kv_lengths", "tree_parents",
+                  "kv_page_table"):
             t = getattr(self, k)
             if t is not None:
                 setattr(c, k, t.cpu())
@@ -113,7 +116,8 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
              causal_kind: str = "none", norm: str = "softmax", qdq: Optional[str] = None,
              qscale: float = 1.0, scale: Optional[float] = None, dist: str = "normal",
              kv_fp8_from: Optional[torch.dtype] = None, device="cpu", name="case",
-             nan_padding: bool = True, tree: Optional[str] = None) -> Case:
+             nan_padding: bool = True, tree: Optional[str] = None, page_size: int = 64,
+             spare_pages: int = 3) -> Case:
     """Draw one operator instance.
 
     q_lens / kv_lens: per-sequence valid lengths (sequences of ints).
@@ -124,6 +128,11 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
       per-tensor fp32 descale s = amax / 448 (the stored code is x / s).
     tree: draft-token parents for tree decoding, token-aligned with Q's rows
       (see ``tree_parents``); None for ordinary attention.
+    kv_form "paged": K and V are drawn as padded [B, H_kv, n_kv, D], then
+      scattered into two pools of pages [P, H_kv, page_size, D] in a random
+      page order (separate for K and V), with ``spare_pages`` extra NaN
+      pages; rows of a last page past the length are NaN, and page-table
+      entries past a sequence's pages point at a NaN page.
     """
     kv_dtype = kv_dtype or dtype
     q_lens = np.asarray(q_lens, dtype=np.int64)
@@ -177,6 +186,9 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
                     t[b, :, :L] = _values(gen, (kv_num_heads, L, D), src_kv_dtype, dist, device)
         return t
 
+    paged = kv_form == "paged"
+    if paged:
+        kv_form = "padded_bhnd"
     k = kv_tensor()
     v = kv_tensor()
     k_descale = v_descale = 1.0
@@ -197,6 +209,11 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
     if pass_kv_lengths is None:
         pass_kv_lengths = True
     query_lengths = torch.from_numpy(ql_cum).to(device) if pass_query_lengths else None
+    kv_page_table = None
+    if paged:
+        k, v, kv_page_table = _to_pages(k, v, kv_lens, page_size, spare_pages, rng)
+        kv_form = "paged"
+        pass_kv_lengths = True
     if kv_form == "packed_nhd":
         kv_lengths = torch.from_numpy(kl_cum).to(device)
     else:
@@ -206,7 +223,7 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
     mask = None
     if mask_kind is not None:
         full = (B, mask_heads, n_q if query_form == "padded_bhnd" else max(1, int(q_lens.max(initial=0))),
-                n_kv if kv_form == "padded_bhnd" else max(1, int(kv_lens.max(initial=0))))
+                n_kv if kv_form != "packed_nhd" else max(1, int(kv_lens.max(initial=0))))
         draw = rng.random(full)
         if mask_kind == "bool":
             m = draw >= mask_p  # True = may attend
@@ -242,7 +259,36 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
                 causal_kind=causal_kind, norm=norm, qdq=qdq, qscale=float(qscale),
                 scale=float(scale), k_descale=float(k_descale), v_descale=float(v_descale),
                 num_heads=num_heads, kv_num_heads=kv_num_heads, q_lens=q_lens, kv_lens=kv_lens,
-                out_dtype=out_dtype, meta=dict(seed=seed), tree_parents=tree_parents)
+                out_dtype=out_dtype, meta=dict(seed=seed), tree_parents=tree_parents,
+                kv_page_table=kv_page_table)
+
+
+def _to_pages(k, v, kv_lens, ps: int, spare: int, rng):
+    """Scatter padded K / V [B, H, n, D] into page pools [P, H, ps, D]:
+    sequence b uses ceil(kv_len_b / ps) pages, K and V in independent random
+    page orders; spare pages and the rows past a length stay NaN.  Returns
+    (k_pool, v_pool, table [B, 2, max_pages] int32 on K's device)."""
+    B, H, n, D = k.shape
+    npages = [(int(L) + ps - 1) // ps for L in kv_lens]
+    used = int(sum(npages))
+    P = used + spare
+    max_pages = max(1, (n + ps - 1) // ps)
+    poison = used  # first spare page: every unused table entry points at it
+    table = np.full((B, 2, max_pages), poison, dtype=np.int32)
+    pools = []
+    for w, src in enumerate((k, v)):
+        pool = _nan_fill((P, H, ps, D), src.dtype, src.device)
+        order = rng.permutation(used)
+        nxt = 0
+        for b in range(B):
+            L = int(kv_lens[b])
+            for p in range(npages[b]):
+                pg = int(order[nxt]); nxt += 1
+                table[b, w, p] = pg
+                rows = min(ps, L - p * ps)
+                pool[pg, :, :rows] = src[b, :, p * ps:p * ps + rows]
+        pools.append(pool)
+    return pools[0], pools[1], torch.from_numpy(table).to(k.device)
 
 
 def tree_parents_for(rng, n: int, kind: str) -> np.ndarray:

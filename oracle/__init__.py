@@ -33,7 +33,7 @@ _DT = {
     torch.uint8: 4,
     torch.float64: 5,
 }
-FORMS = {"padded_bhnd": 0, "packed_nhd": 1}
+FORMS = {"padded_bhnd": 0, "packed_nhd": 1, "paged": 2}
 CAUSAL = {"none": 0, "upper_left": 1, "lower_right": 2}
 NORM = {"softmax": 0, "none": 1}
 QDQ = {None: 0, "off": 0, "fp8": 1, "int8": 2}
@@ -71,6 +71,8 @@ class _Args(ctypes.Structure):
         ("kv_num_heads", ctypes.c_int32),
         ("amb_rel", ctypes.c_double),
         ("tree_parents", ctypes.c_void_p),
+        ("kv_page_table", ctypes.c_void_p),
+        ("kv_max_pages", ctypes.c_int32),
     ]
 
 
@@ -176,6 +178,8 @@ def _args(q, k, v, mask, query_lengths, kv_lengths, batch, query_form, kv_form, 
     a.kv_num_heads = kv_num_heads
     a.amb_rel = amb_rel
     a.tree_parents = None
+    a.kv_page_table = None
+    a.kv_max_pages = 0
     return a
 
 
@@ -197,13 +201,15 @@ def attention(q, k, v, mask=None, *, query_lengths=None, kv_lengths=None, batch=
               query_form="padded_bhnd", kv_form="padded_bhnd", causal_kind="none",
               norm="softmax", qdq=None, qscale=1.0, scale=1.0, k_descale=1.0, v_descale=1.0,
               num_heads=None, kv_num_heads=None, rows=None, amb_rel=1e-5,
-              tree_parents=None) -> OracleResult:
+              tree_parents=None, kv_page_table=None) -> OracleResult:
     """Evaluate the operator on host tensors (raw storage dtypes).
 
     ``rows`` selects output rows (b, h, i); default is every valid row.
     ``num_heads`` / ``kv_num_heads`` default to Q's / K's head dimension.
     ``tree_parents``: int32 parent index of each query row's draft token
     (token-aligned with Q's rows: [T_q] packed, [B, N_q] padded), or None.
+    ``kv_page_table``: int32 [B, 2, max_pages] for kv_form "paged" (K and V
+    are then page pools [P, H_kv, page_size, D]).
     """
     if num_heads is None:
         num_heads = q.shape[1]
@@ -217,6 +223,11 @@ def attention(q, k, v, mask=None, *, query_lengths=None, kv_lengths=None, batch=
         tp = torch.as_tensor(tree_parents).to("cpu", torch.int32).contiguous()
         keep.append(tp)
         a.tree_parents = tp.data_ptr()
+    if kv_page_table is not None:
+        pt = torch.as_tensor(kv_page_table).to("cpu", torch.int32).contiguous()
+        keep.append(pt)
+        a.kv_page_table = pt.data_ptr()
+        a.kv_max_pages = pt.shape[-1]
     lib = _load()
     if rows is None:
         n = lib.oracle_count_rows(ctypes.byref(a))

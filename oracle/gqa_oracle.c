@@ -50,6 +50,14 @@
  * (j < kv_len_b - q_len_b) and the drafts on its own ancestor chain, itself
  * included; this rule is ANDed with the causal kind and the mask.
  *
+ * Paged KV (TensorRT Edge-LLM "TensorRT Plugins Guide", AttentionPlugin
+ * decoder tensor contract: kv_page_table [N, 2, max_pages_per_sequence], a
+ * page-table view into resident paged KV pools).  K and V are pools of
+ * pages [P, H_kv, page_size, D]; key j of sequence b is row j % page_size
+ * of page kv_page_table[b][0][j / page_size] of the K pool, and of page
+ * kv_page_table[b][1][j / page_size] of the V pool; kv_lengths [B] gives
+ * the sequence lengths.
+ *
  * Alongside O the oracle returns, per output element, the largest change a
  * different rounding of "ambiguous" quantization inputs could make
  * (|x - nearest rounding midpoint| <= amb_rel * |x|), so that a GPU result
@@ -62,7 +70,7 @@
 
 /* ---- dtype codes private to the oracle ------------------------------- */
 enum { OR_F16 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F32 = 3, OR_BOOL = 4, OR_F64 = 5 };
-enum { OR_PADDED = 0, OR_PACKED = 1 };
+enum { OR_PADDED = 0, OR_PACKED = 1, OR_PAGED = 2 };
 enum { OR_CAUSAL_NONE = 0, OR_CAUSAL_UPPER_LEFT = 1, OR_CAUSAL_LOWER_RIGHT = 2 };
 enum { OR_NORM_SOFTMAX = 0, OR_NORM_NONE = 1 };
 enum { OR_QDQ_OFF = 0, OR_QDQ_FP8 = 1, OR_QDQ_INT8 = 2 };
@@ -86,6 +94,8 @@ typedef struct {
     int32_t num_heads, kv_num_heads;
     double amb_rel;
     const int32_t* tree_parents; /* [T_q] (packed Q) or [B, N_q] (padded Q), or NULL */
+    const int32_t* kv_page_table; /* paged KV: [B, 2, kv_max_pages] */
+    int32_t kv_max_pages;
 } or_args;
 
 /* ---- exact decoding of the storage formats -------------------------- */
@@ -190,6 +200,7 @@ static int64_t q_len_of(const or_args* a, int b) {
 }
 static int64_t kv_len_of(const or_args* a, int b) {
     if (a->kv_form == OR_PACKED) return (int64_t)a->kv_lengths[b + 1] - a->kv_lengths[b];
+    if (a->kv_form == OR_PAGED) return a->kv_lengths[b];
     if (a->kv_lengths) return a->kv_lengths[b];
     return a->k.shape[2];
 }
@@ -198,6 +209,15 @@ static int64_t row_off(const or_tensor* t, int form, const int32_t* cum, int b, 
     if (form == OR_PACKED)
         return ((int64_t)cum[b] + i) * t->stride[0] + (int64_t)head * t->stride[1];
     return (int64_t)b * t->stride[0] + (int64_t)head * t->stride[1] + i * t->stride[2];
+}
+/* Offset (elements) of key row (b, kv head, j) of K (which = 0) or V (1);
+ * paged KV looks the page up in the page table. */
+static int64_t kv_row_off(const or_args* a, int which, int b, int head, int64_t j) {
+    const or_tensor* t = which ? &a->v : &a->k;
+    if (a->kv_form != OR_PAGED) return row_off(t, a->kv_form, a->kv_lengths, b, head, j);
+    const int64_t ps = t->shape[2];
+    const int32_t page = a->kv_page_table[((int64_t)b * 2 + which) * a->kv_max_pages + j / ps];
+    return (int64_t)page * t->stride[0] + (int64_t)head * t->stride[1] + (j % ps) * t->stride[2];
 }
 /* Mask element (b, h, i, j): right-aligned broadcast, size-1 dims stride 0. */
 static int64_t mask_off(const or_tensor* m, int b, int h, int64_t i, int64_t j) {
@@ -235,6 +255,14 @@ static int rows_in_bounds(const or_args* a, int b, int64_t ql, int64_t kl) {
     } else if (ql > a->q.shape[2] || b >= a->q.shape[0]) return 0;
     if (a->kv_form == OR_PACKED) {
         if ((int64_t)a->kv_lengths[b] + kl > a->k.shape[0]) return 0;
+    } else if (a->kv_form == OR_PAGED) {
+        const int64_t ps = a->k.shape[2];
+        if (!a->kv_page_table || ps != a->v.shape[2] || kl > (int64_t)a->kv_max_pages * ps) return 0;
+        for (int64_t p = 0; p * ps < kl; ++p)
+            for (int w = 0; w < 2; ++w) {
+                const int32_t pg = a->kv_page_table[((int64_t)b * 2 + w) * a->kv_max_pages + p];
+                if (pg < 0 || pg >= (w ? a->v.shape[0] : a->k.shape[0])) return 0;
+            }
     } else if (kl > a->k.shape[2] || b >= a->k.shape[0]) return 0;
     if (a->mask.data) {
         int64_t need[4] = {b + 1, a->num_heads, ql, kl};
@@ -323,7 +351,7 @@ int oracle_rows(const or_args* a, const int32_t* rows, int64_t nrows, double* ou
             }
             ok[j] = (char)allowed;
             if (!allowed) { s[j] = 0.0; continue; }
-            const int64_t ko = row_off(&a->k, a->kv_form, a->kv_lengths, b, g, j);
+            const int64_t ko = kv_row_off(a, 0, b, g, j);
             double dot = 0.0;
             for (int64_t d = 0; d < D; ++d)
                 dot += load_elem(&a->q, qo + d * a->q.stride[a->query_form == OR_PACKED ? 2 : 3]) *
@@ -352,7 +380,7 @@ int oracle_rows(const or_args* a, const int32_t* rows, int64_t nrows, double* ou
             double p = s[j], delta = 0.0;
             if (a->qdq == OR_QDQ_FP8) p = q_fp8(p / qs, a->amb_rel, &delta) * qs;
             else if (a->qdq == OR_QDQ_INT8) p = q_int8(p / qs, a->amb_rel, &delta) * qs;
-            const int64_t vo = row_off(&a->v, a->kv_form, a->kv_lengths, b, g, j);
+            const int64_t vo = kv_row_off(a, 1, b, g, j);
             const int64_t vs = a->v.stride[a->kv_form == OR_PACKED ? 2 : 3];
             for (int64_t d = 0; d < D; ++d) {
                 double vv = load_elem(&a->v, vo + d * vs) * vd;

@@ -71,9 +71,22 @@ def dense(case) -> tuple[np.ndarray, np.ndarray]:
                 out[b, :, :L] = x[b, :, :L]
         return out
 
+    def unpage(x, w):
+        # paged KV: key j of sequence b is row j % ps of page table[b, w, j // ps]
+        ps = x.shape[2]
+        tab = case.kv_page_table.cpu().numpy()
+        out = np.zeros((B, x.shape[1], nk, D))
+        for b in range(B):
+            for jj in range(int(kl[b])):
+                out[b, :, jj] = x[tab[b, w, jj // ps], :, jj % ps]
+        return out
+
     Q = unpack(q, case.query_form, ql, nq)                 # [B, Hq, nq, D]
-    K = unpack(k, case.kv_form, kl, nk)                    # [B, Hkv, nk, D]
-    V = unpack(v, case.kv_form, kl, nk)
+    if case.kv_form == "paged":
+        K, V = unpage(k, 0), unpage(v, 1)
+    else:
+        K = unpack(k, case.kv_form, kl, nk)                # [B, Hkv, nk, D]
+        V = unpack(v, case.kv_form, kl, nk)
     G = Hq // Hkv
     K = np.repeat(K, G, axis=1)
     V = np.repeat(V, G, axis=1)

@@ -46,8 +46,26 @@ def subcase(case, bs):
         return torch.stack([t[b].cpu() for b in bs])
 
     q = take(c.q, c.query_form, c.q_lens)
-    k = take(c.k, c.kv_form, c.kv_lens)
-    v = take(c.v, c.kv_form, c.kv_lens)
+    table = None
+    if c.kv_form == "paged":
+        # the sequences' own pages only, renumbered in a compact pool
+        ps = c.k.shape[2]
+        tab = c.kv_page_table.cpu()
+        table = torch.zeros((len(bs), 2, tab.shape[2]), dtype=torch.int32)
+        pools = []
+        for w, src in enumerate((c.k, c.v)):
+            ids = []
+            for n, b in enumerate(bs):
+                cnt = (int(c.kv_lens[b]) + ps - 1) // ps
+                table[n, w, :cnt] = torch.arange(len(ids), len(ids) + cnt, dtype=torch.int32)
+                ids += [int(x) for x in tab[b, w, :cnt]]
+            if not ids:
+                ids = [0]
+            pools.append(src[torch.tensor(ids, device=src.device)].cpu())
+        k, v = pools
+    else:
+        k = take(c.k, c.kv_form, c.kv_lens)
+        v = take(c.v, c.kv_form, c.kv_lens)
     mask = None
     if c.mask is not None:
         m = c.mask
@@ -77,6 +95,7 @@ def subcase(case, bs):
     sub = synth.Case(**{f: getattr(c, f) for f in c.__dataclass_fields__})
     sub.q, sub.k, sub.v, sub.mask = q, k, v, mask
     sub.tree_parents = tree
+    sub.kv_page_table = table
     sub.query_lengths, sub.kv_lengths = query_lengths, kv_lengths
     sub.batch = len(bs)
     sub.q_lens, sub.kv_lens = ql, kl
