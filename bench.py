@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}  # dense MFMA TFLOP/s
 HBM_PEAK = 8000.0  # GB/s
-WORKLOADS = ("2", "3", "4a", "4b", "5a", "5b", "tree", "kvu", "1")
+WORKLOADS = ("2", "3", "4a", "4b", "4p", "5a", "5b", "tree", "kvu", "1")
 KERNEL_SOURCES = {
     "prefill": ["gqa_attention_ragged_amd/csrc/prefill.hip",
                 "gqa_attention_ragged_amd/csrc/prefill_impl.h",

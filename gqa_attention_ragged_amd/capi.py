@@ -26,7 +26,7 @@ DTYPES = {
     torch.bool: 4,
     torch.uint8: 4,
 }
-FORMS = {"padded_bhnd": 0, "packed_nhd": 1}
+FORMS = {"padded_bhnd": 0, "packed_nhd": 1, "paged": 2}
 CAUSAL = {"none": 0, "upper_left": 1, "lower_right": 2}
 NORM = {"softmax": 0, "none": 1}
 QDQ = {None: 0, "off": 0, "fp8": 1, "int8": 2}
@@ -64,6 +64,8 @@ class GqaArgs(ctypes.Structure):
         ("num_heads", ctypes.c_int32),
         ("kv_num_heads", ctypes.c_int32),
         ("tree_parents", ctypes.c_void_p),
+        ("kv_page_table", ctypes.c_void_p),
+        ("kv_max_pages", ctypes.c_int32),
     ]
 
 
@@ -150,14 +152,15 @@ def tensor_view(t: Optional[torch.Tensor]) -> GqaTensor:
 def make_args(q, k, v, attn_mask=None, out=None, *, query_lengths=None, kv_lengths=None,
               batch=None, query_form="padded_bhnd", kv_form="padded_bhnd", causal_kind="none",
               norm="softmax", qdq=None, qscale=1.0, scale=1.0, k_descale=1.0, v_descale=1.0,
-              num_heads=None, kv_num_heads=None, tree_parents=None) -> GqaArgs:
+              num_heads=None, kv_num_heads=None, tree_parents=None,
+              kv_page_table=None) -> GqaArgs:
     """Fill a gqa_attn_args_t from tensors (no copies, no checks)."""
     a = GqaArgs()
     a.q, a.k, a.v = tensor_view(q), tensor_view(k), tensor_view(v)
     a.attn_mask = tensor_view(attn_mask)
     a.out = tensor_view(out)
     for name, t in (("query_lengths", query_lengths), ("kv_lengths", kv_lengths),
-                    ("tree_parents", tree_parents)):
+                    ("tree_parents", tree_parents), ("kv_page_table", kv_page_table)):
         if t is not None and t.dtype != torch.int32:
             raise ValueError(f"{name} must be int32")
         setattr(a, name, None if t is None else t.data_ptr())
@@ -169,6 +172,7 @@ def make_args(q, k, v, attn_mask=None, out=None, *, query_lengths=None, kv_lengt
         else:
             batch = query_lengths.numel() - 1
     a.batch = batch
+    a.kv_max_pages = 0 if kv_page_table is None else kv_page_table.shape[-1]
     a.query_form = FORMS[query_form]
     a.kv_form = FORMS[kv_form]
     a.causal_kind = CAUSAL[causal_kind]

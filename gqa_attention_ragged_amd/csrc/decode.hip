@@ -65,7 +65,7 @@ __device__ __forceinline__ u32x2 lds_tr8(const char* p) {
                                          (__attribute__((address_space(3))) i32x2*)(p)));
 }
 
-template <typename TQ, typename TKV, int D>
+template <typename TQ, typename TKV, int D, bool PAGED = false>
 struct Decode {
     static constexpr bool KV8 = std::is_same<TKV, fp8>::value;
     static constexpr int KES = KV8 ? 1 : 2;       // K/V element bytes
@@ -125,10 +125,11 @@ struct Decode {
                 qreg[ks] = a;
             }
         }
-        const char* kbase =
-            (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * KES;
-        const char* vbase =
-            (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * KES;
+        // paged KV: the head's offset inside a page (the page comes per tile)
+        const int64_t kro = PAGED ? 0 : kv_rowbase(p, p.k, b), vro = PAGED ? 0 : kv_rowbase(p, p.v, b);
+        const char* kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * KES;
+        const char* vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * KES;
+        const int32_t* ptk = p.ptab + (int64_t)b * 2 * p.ptab_pages;
         char* sv = smem + wave * WAVE_LDS;
         const float sc = p.scale * p.k_descale * kLog2e;
 
@@ -154,6 +155,35 @@ struct Decode {
         const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, rows_bytes(k1, p.k.sn, D, KES));
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, rows_bytes(k1, p.v.sn, D, KES));
         auto load = [&](Tile& t, int j0) {
+            if constexpr (PAGED) {
+                // a 32-key tile lies inside one page (pages hold a power of
+                // two >= 32 keys); the table is read at a clamped index, and
+                // a tile past the split's end gets an empty range
+                const int pi = min(j0, k1 - 1) >> p.page_shift;
+                const int within = j0 & ((1 << p.page_shift) - 1);
+                const int valid = min(k1 - j0, KT);
+                const int pk = ptk[pi], pv = ptk[p.ptab_pages + pi];
+                const __amdgpu_buffer_rsrc_t kt = make_rsrc(
+                    kbase + ((int64_t)pk * p.k.sb + (int64_t)within * p.k.sn) * KES,
+                    rows_bytes(valid, p.k.sn, D, KES));
+                const __amdgpu_buffer_rsrc_t vt = make_rsrc(
+                    vbase + ((int64_t)pv * p.v.sb + (int64_t)within * p.v.sn) * KES,
+                    rows_bytes(valid, p.v.sn, D, KES));
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int jj = kb * 16 + l16;
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks)
+                        buf_load(kt, (uint32_t)(((int64_t)jj * p.k.sn + ks * 32 + g * 8) * KES),
+                                 t.k[kb][ks]);
+                }
+#pragma unroll
+                for (int i = 0; i < VINS; ++i) {
+                    const int jj = i * VRPI + vrow;
+                    buf_load(vt, (uint32_t)((int64_t)jj * p.v.sn * KES + vch * 16), t.v[i]);
+                }
+                return;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int j = j0 + kb * 16 + l16;
@@ -304,9 +334,9 @@ struct Decode {
     }
 };
 
-template <typename TQ, typename TKV, int D>
+template <typename TQ, typename TKV, int D, bool PAGED>
 __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnParams p) {
-    typedef Decode<TQ, TKV, D> K;
+    typedef Decode<TQ, TKV, D, PAGED> K;
     __shared__ __attribute__((aligned(16))) char smem[K::LDS_BYTES];
     K::run(p, smem);
 }
@@ -335,8 +365,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(AttnParams p) {
 
 template <typename TQ, typename TKV, int D>
 static hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_split_kernel<TQ, TKV, D>), dim3(p.hkv, p.batch, p.n_splits),
-                       dim3(256), 0, stream, p);
+    if (p.kv_paged)
+        hipLaunchKernelGGL((decode_split_kernel<TQ, TKV, D, true>), dim3(p.hkv, p.batch, p.n_splits),
+                           dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<TQ, TKV, D, false>), dim3(p.hkv, p.batch, p.n_splits),
+                           dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<TQ, D>), dim3(p.hq, p.batch), dim3(D), 0, stream, p);

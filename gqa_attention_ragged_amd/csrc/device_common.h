@@ -57,6 +57,10 @@ struct AttnParams {
     int32_t split_keys, n_splits;
     int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs
     const int32_t* tree;              // draft-token parents, token-aligned with Q's rows, or null
+    // paged KV: k / v are page pools [P, H_kv, 2^page_shift, D]; ptab is the
+    // page table [B, 2, ptab_pages] (K pages, then V pages, per sequence)
+    const int32_t* ptab;
+    int32_t ptab_pages, page_shift, kv_paged;
 };
 
 // ---------------------------------------------------------------- lengths

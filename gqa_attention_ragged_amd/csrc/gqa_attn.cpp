@@ -84,9 +84,13 @@ int check_tensor(const gqa_tensor_t& t, const char* name, int form) {
 
 int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     if (!a) return fail(GQA_ERR_INVALID_ARG, "args is null");
-    const int qf = a->query_form, kf = a->kv_form;
-    if ((qf != 0 && qf != 1) || (kf != 0 && kf != 1))
-        return fail(GQA_ERR_INVALID_ARG, "query_form / kv_form must be 0 or 1");
+    const int qf = a->query_form;
+    if ((qf != 0 && qf != 1) || (a->kv_form < 0 || a->kv_form > 2))
+        return fail(GQA_ERR_INVALID_ARG, "query_form must be 0 or 1, kv_form 0, 1 or 2");
+    // paged KV pools are rank-4 like the padded form; kf is the addressing
+    // form used below (paged addressing is selected by `paged`)
+    const bool paged = a->kv_form == GQA_FORM_PAGED;
+    const int kf = paged ? GQA_FORM_PADDED_BHND : a->kv_form;
     if (a->causal_kind < 0 || a->causal_kind > 2)
         return fail(GQA_ERR_INVALID_ARG, "causal_kind must be 0, 1 or 2");
     if (a->norm != GQA_NORM_SOFTMAX && a->norm != GQA_NORM_NONE)
@@ -131,15 +135,31 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     if (B < 0) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0");
     if (qf == GQA_FORM_PADDED_BHND && a->q.shape[0] != B)
         return fail(GQA_ERR_INVALID_ARG, "batch != q.shape[0]");
-    if (kf == GQA_FORM_PADDED_BHND && a->k.shape[0] != B)
+    if (kf == GQA_FORM_PADDED_BHND && !paged && a->k.shape[0] != B)
         return fail(GQA_ERR_INVALID_ARG, "batch != k.shape[0]");
+    int page_shift = 0;
+    if (paged) {
+        if (!a->kv_lengths) return fail(GQA_ERR_INVALID_ARG, "kv_lengths is required for paged KV");
+        if (!a->kv_page_table || a->kv_max_pages < 1)
+            return fail(GQA_ERR_INVALID_ARG, "paged KV needs kv_page_table and kv_max_pages >= 1");
+        const int64_t ps = a->k.shape[2];
+        while (page_shift < 30 && (int64_t{1} << page_shift) < ps) ++page_shift;
+        if (ps < 32 || (int64_t{1} << page_shift) != ps)
+            return fail(GQA_ERR_UNSUPPORTED, "page_size must be a power of two >= 32");
+        if ((int64_t)a->kv_max_pages * ps > INT32_MAX)
+            return fail(GQA_ERR_UNSUPPORTED, "kv_max_pages * page_size beyond int32");
+    } else if (a->kv_page_table) {
+        return fail(GQA_ERR_INVALID_ARG, "kv_page_table given without the paged KV form");
+    }
     if (qf == GQA_FORM_PACKED_NHD && !a->query_lengths)
         return fail(GQA_ERR_INVALID_ARG, "query_lengths is required for packed_nhd Q");
     if (kf == GQA_FORM_PACKED_NHD && !a->kv_lengths)
         return fail(GQA_ERR_INVALID_ARG, "kv_lengths is required for packed_nhd KV");
 
     const int64_t Nq = qf == GQA_FORM_PADDED_BHND ? a->q.shape[2] : 0;
-    const int64_t Nkv = kf == GQA_FORM_PADDED_BHND ? a->k.shape[2] : 0;
+    // paged: the logical key extent of a sequence is kv_max_pages pages
+    const int64_t Nkv = paged ? (int64_t)a->kv_max_pages * a->k.shape[2]
+                              : (kf == GQA_FORM_PADDED_BHND ? a->k.shape[2] : 0);
     const int64_t Tq = qf == GQA_FORM_PACKED_NHD ? a->q.shape[0] : 0;
     const int64_t Tkv = kf == GQA_FORM_PACKED_NHD ? a->k.shape[0] : 0;
     const int64_t kv_max = kf == GQA_FORM_PADDED_BHND ? Nkv : Tkv;
@@ -204,6 +224,11 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         return fail(GQA_ERR_UNSUPPORTED,
                     "an fp8 KV cache with 16-bit Q is supported for the decode step "
                     "(padded Q with N_q = 1, softmax, no mask, no Q/DQ, causal none/lower_right)");
+    if (paged && !decode &&
+        (a->norm != GQA_NORM_SOFTMAX || a->qdq != GQA_QDQ_OFF || a->k.shape[2] < 64))
+        return fail(GQA_ERR_UNSUPPORTED,
+                    "paged KV beyond the decode step needs softmax without Q/DQ and pages of "
+                    ">= 64 keys");
 
     // common parameters
     auto view = [](const gqa_tensor_t& t, int form) {
@@ -233,6 +258,10 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // With one query row per sequence (the decode step) the row is its own
     // only draft and the tree rule allows every key: the tree has no effect.
     p.tree = a->tree_parents;
+    p.kv_paged = paged;
+    p.ptab = a->kv_page_table;
+    p.ptab_pages = paged ? a->kv_max_pages : 0;
+    p.page_shift = page_shift;
     p.q_packed = qf;
     p.kv_packed = kf;
     p.batch = (int)B;
@@ -298,7 +327,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // 32 rows; with tree decoding a mask is read per lane (the generic
     // variant carries the tree rule).
     p.mask_lds = 0;
-    if (m.data && !a->tree_parents && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
+    if (m.data && !a->tree_parents && !paged && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
         (p.mask_kind == gqa::MASK_BOOL || p.mask_kind == gqa::MASK_F16 ||
          p.mask_kind == gqa::MASK_BF16)) {
         const int64_t es = p.mask_kind == gqa::MASK_BOOL ? 1 : 2;
@@ -513,6 +542,6 @@ const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_last_hip_error(void) { return g_hip_err; }
 
-int gqa_attn_abi_version(void) { return 3; }
+int gqa_attn_abi_version(void) { return 4; }
 
 }  // extern "C"

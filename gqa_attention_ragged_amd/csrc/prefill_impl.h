@@ -150,7 +150,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // generic and tree variants (a tree with a mask takes the generic one).
 enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3, MK_TREE = 4 };
 
-template <typename TI, int D, int MK>
+template <typename TI, int D, int MK, bool PAGED = false>
 struct Prefill {
     static constexpr bool HAS_MASK = MK != MK_NONE && MK != MK_TREE;
     static constexpr bool TREE = MK == MK_GENERIC || MK == MK_TREE;  // tree rule compiled in
@@ -278,9 +278,27 @@ struct Prefill {
     // the lane was given for that position (padding lanes of K get an offset
     // beyond the range: zeros, no memory access).  Completion is waited for
     // with vmcnt before the barrier that publishes the stage.
-    __device__ __forceinline__ static void dma_tile(const Ctx& c, int tile, bool with_v,
-                                                    char* stage, int wave) {
-        const __amdgpu_buffer_rsrc_t kr = window(c.kbase, c.kbytes, c.ktile, tile);
+    __device__ __forceinline__ static void dma_tile(const AttnParams& p, const Ctx& c, int tile,
+                                                    bool with_v, char* stage, int wave) {
+        __amdgpu_buffer_rsrc_t kr, vr;
+        if constexpr (PAGED) {
+            // the tile lies inside one page (pages hold a power of two >= BN
+            // keys): its base comes from the page table, its range ends
+            // with the sequence's last valid key
+            const int row0 = tile * C::BN;
+            const int pi = row0 >> p.page_shift;
+            const int within = row0 & ((1 << p.page_shift) - 1);
+            const uint32_t valid = rows_bytes(min(C::BN, c.kv_len - row0), p.k.sn, D, C::ES);
+            const int32_t* pt = p.ptab + (int64_t)c.b * 2 * p.ptab_pages + pi;
+            kr = make_rsrc(c.kbase + ((int64_t)pt[0] * p.k.sb + (int64_t)within * p.k.sn) * C::ES,
+                           valid);
+            vr = make_rsrc(c.vbase + ((int64_t)pt[p.ptab_pages] * p.v.sb +
+                                      (int64_t)within * p.v.sn) * C::ES,
+                           rows_bytes(min(C::BN, c.kv_len - row0), p.v.sn, D, C::ES));
+        } else {
+            kr = window(c.kbase, c.kbytes, c.ktile, tile);
+            vr = window(c.vbase, c.vbytes, c.vtile, tile);
+        }
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) {
             const int j = wave + 4 * k;
@@ -288,7 +306,6 @@ struct Prefill {
             buf_load_lds16(kr, stage + dst, c.koff[k]);
         }
         if (!with_v) return;
-        const __amdgpu_buffer_rsrc_t vr = window(c.vbase, c.vbytes, c.vtile, tile);
 #pragma unroll
         for (int k = 0; k < C::VMAX; ++k) {
             const int j = wave + 4 * k;
@@ -534,7 +551,7 @@ struct Prefill {
             if constexpr (PRIMED) {
                 if (mlds) store_mask(st0, c, rm0);
             } else {
-                dma_tile(c, c.t0, with_v, st0, wave);
+                dma_tile(p, c, c.t0, with_v, st0, wave);
                 if (mlds) load_mask(p, c, c.t0, rm);
                 if (mlds) store_mask(st0, c, rm);
             }
@@ -546,7 +563,7 @@ struct Prefill {
         // addresses are compile-time LDS offsets.
         auto body = [&](int it, char* __restrict__ stage, char* __restrict__ nstage) {
             const bool more = it + 1 < c.t1;
-            if (more) dma_tile(c, it + 1, with_v, nstage, wave);
+            if (more) dma_tile(p, c, it + 1, with_v, nstage, wave);
             if (mlds && more) load_mask(p, c, it + 1, rm);
             const int j0 = it * C::BN;
             if (c.wave_rows && j0 < c.wave_kv_end) {
@@ -768,8 +785,10 @@ struct Prefill {
         const int wave_last = min(c.wr0 + 32, c.q_len) - 1;
         c.wave_kv_end = c.kv_len;
         if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
-        c.kbase = (const char*)p.k.ptr + (kv_rowbase(p, p.k, b) + (int64_t)kvh * p.k.sh) * C::ES;
-        c.vbase = (const char*)p.v.ptr + (kv_rowbase(p, p.v, b) + (int64_t)kvh * p.v.sh) * C::ES;
+        // paged KV: the head's offset inside a page (the page comes per tile)
+        const int64_t kro = PAGED ? 0 : kv_rowbase(p, p.k, b), vro = PAGED ? 0 : kv_rowbase(p, p.v, b);
+        c.kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * C::ES;
+        c.vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * C::ES;
         c.kbytes = rows_bytes(c.kv_len, p.k.sn, D, C::ES);
         c.vbytes = rows_bytes(c.kv_len, p.v.sn, D, C::ES);
         c.ktile = (uint32_t)((int64_t)C::BN * p.k.sn * C::ES);
@@ -835,7 +854,7 @@ struct Prefill {
         constexpr bool kFirstWithV = MODE != MODE_SOFTMAX_QDQ && MODE != MODE_SOFTMAX_QDQ_NS;
         u32x4 rm0 = {};
         if (c.t0 < c.t1) {
-            dma_tile(c, c.t0, kFirstWithV, st0, wave);
+            dma_tile(p, c, c.t0, kFirstWithV, st0, wave);
             if constexpr (STAGED) load_mask(p, c, c.t0, rm0);
         }
 
@@ -937,15 +956,15 @@ struct Prefill {
     }
 };
 
-template <typename TI, int D, int MODE, int MK>
+template <typename TI, int D, int MODE, int MK, bool PAGED = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
     // two separate stage arrays: the compiler then knows that the copy into
     // one stage never aliases the reads of the other, and does not wait for
     // the copy before computing on the current stage
-    typedef Prefill<TI, D, MK> P;
+    typedef Prefill<TI, D, MK, PAGED> P;
     __shared__ __attribute__((aligned(16))) char st0[P::SSTAGE + P::SPARE];
     __shared__ __attribute__((aligned(16))) char st1[P::SSTAGE + P::SPARE];
-    Prefill<TI, D, MK>::template run<MODE>(p, st0, st1);
+    P::template run<MODE>(p, st0, st1);
 }
 
 // Split-KV combine: one workgroup per (row tile, query head) merges the
@@ -999,6 +1018,22 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
 template <typename TI, int D, int MODE>
 static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
+    if constexpr (MODE == MODE_SOFTMAX && !std::is_same<TI, fp8>::value) {
+        // paged KV: online softmax only (host-checked); masks are read per
+        // lane (generic variant)
+        if (p.kv_paged) {
+            if (p.mask_kind != MASK_NONE)
+                hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_GENERIC, true>), grid, dim3(256),
+                                   0, stream, p);
+            else if (p.tree)
+                hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_TREE, true>), grid, dim3(256), 0,
+                                   stream, p);
+            else
+                hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_NONE, true>), grid, dim3(256), 0,
+                                   stream, p);
+            return;
+        }
+    }
     if (p.mask_kind == MASK_NONE && p.tree)
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_TREE>), grid, dim3(256), 0, stream, p);
     else if (p.mask_kind == MASK_NONE)

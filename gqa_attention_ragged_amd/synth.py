@@ -189,6 +189,7 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
     paged = kv_form == "paged"
     if paged:
         kv_form = "padded_bhnd"
+        n_kv = -(-n_kv // page_size) * page_size  # whole pages
     k = kv_tensor()
     v = kv_tensor()
     k_descale = v_descale = 1.0
@@ -264,29 +265,33 @@ def generate(*, seed: int, q_lens, kv_lens, num_heads: int, kv_num_heads: int, h
 
 
 def _to_pages(k, v, kv_lens, ps: int, spare: int, rng):
-    """Scatter padded K / V [B, H, n, D] into page pools [P, H, ps, D]:
-    sequence b uses ceil(kv_len_b / ps) pages, K and V in independent random
-    page orders; spare pages and the rows past a length stay NaN.  Returns
-    (k_pool, v_pool, table [B, 2, max_pages] int32 on K's device)."""
+    """Scatter padded K / V [B, H, n, D] (n a multiple of ps) into page pools
+    [P, H, ps, D]: sequence b uses ceil(kv_len_b / ps) pages, K and V in
+    independent random page orders; spare pages and the rows past a length
+    stay NaN.  Returns (k_pool, v_pool, table [B, 2, max_pages] int32 on K's
+    device)."""
     B, H, n, D = k.shape
-    npages = [(int(L) + ps - 1) // ps for L in kv_lens]
-    used = int(sum(npages))
+    assert n % ps == 0
+    npages = np.array([(int(L) + ps - 1) // ps for L in kv_lens], dtype=np.int64)
+    used = int(npages.sum())
     P = used + spare
-    max_pages = max(1, (n + ps - 1) // ps)
+    max_pages = max(1, n // ps)
     poison = used  # first spare page: every unused table entry points at it
     table = np.full((B, 2, max_pages), poison, dtype=np.int32)
+    b_idx = np.repeat(np.arange(B), npages)
+    p_idx = np.concatenate([np.arange(c) for c in npages]) if used else np.zeros(0, np.int64)
     pools = []
     for w, src in enumerate((k, v)):
         pool = _nan_fill((P, H, ps, D), src.dtype, src.device)
         order = rng.permutation(used)
-        nxt = 0
-        for b in range(B):
-            L = int(kv_lens[b])
-            for p in range(npages[b]):
-                pg = int(order[nxt]); nxt += 1
-                table[b, w, p] = pg
-                rows = min(ps, L - p * ps)
-                pool[pg, :, :rows] = src[b, :, p * ps:p * ps + rows]
+        table[b_idx, w, p_idx] = order
+        if used:
+            pages = src.view(B, H, n // ps, ps, D)
+            bi = torch.from_numpy(b_idx).to(src.device)
+            pi = torch.from_numpy(p_idx).to(src.device)
+            flat = pool.view(torch.uint8) if src.dtype == FP8 else pool
+            srcv = pages.view(torch.uint8) if src.dtype == FP8 else pages
+            flat[torch.from_numpy(order).to(src.device)] = srcv[bi, :, pi]
         pools.append(pool)
     return pools[0], pools[1], torch.from_numpy(table).to(k.device)
 
@@ -356,7 +361,7 @@ def _to_fp8_per_tensor(x: torch.Tensor, form: str, lens) -> tuple[torch.Tensor, 
 # The five workload configurations (LLM-shaped prefill, chunked context,
 # decode and quantized attention), at their full sizes.
 # --------------------------------------------------------------------------
-CONFIGS = ("1", "2", "3", "4a", "4b", "5a", "5b", "tree")
+CONFIGS = ("1", "2", "3", "4a", "4b", "4p", "5a", "5b", "tree")
 
 DESCRIPTIONS = {
     "1": "tiny padded MHA fp16 B=2 H=4 N=128 D=64",
@@ -364,6 +369,7 @@ DESCRIPTIONS = {
     "3": "packed Q / padded KV chunked context fp16 B=8 q~U[1,512] Nkv=8192 + additive mask",
     "4a": "decode fp16 KV B=128 Nkv=32768 kv~U[512,32768] Hq=32 Hkv=8 D=128",
     "4b": "decode fp8 e4m3 KV (per-tensor fp32 descale) B=128 Nkv=32768 Hq=32 Hkv=8 D=128",
+    "4p": "decode fp16 KV in 64-key pages (paged KV) B=128 kv~U[512,32768] Hq=32 Hkv=8 D=128",
     "5a": "quantized attention fp8 Q/K/V B=4 N=4096 Hq=32 Hkv=8 D=128 causal, P fp8 Q/DQ 1/448",
     "5b": "quantized attention as 5a plus bool mask [4,1,4096,4096] 90% true",
     "tree": ("tree (speculative) decoding fp16 B=32, 64 draft tokens per sequence in a "
@@ -373,7 +379,7 @@ DESCRIPTIONS = {
 
 def config_lengths(cfg: str):
     """(q_lens, kv_lens) of a configuration (drawn first from its seed)."""
-    seed = {"1": 1, "2": 2, "3": 3, "4a": 4, "4b": 4, "5a": 5, "5b": 5, "tree": 6}[cfg]
+    seed = {"1": 1, "2": 2, "3": 3, "4a": 4, "4b": 4, "4p": 4, "5a": 5, "5b": 5, "tree": 6}[cfg]
     rng = np.random.Generator(np.random.PCG64(seed))
     if cfg == "1":
         return np.full(2, 128), np.full(2, 128)
@@ -384,7 +390,7 @@ def config_lengths(cfg: str):
         q = rng.integers(1, 513, size=8)
         kv = np.array([rng.integers(int(a), 8193) for a in q])
         return q, kv
-    if cfg in ("4a", "4b"):
+    if cfg in ("4a", "4b", "4p"):
         kv = rng.integers(512, 32769, size=128)
         return np.ones(128, dtype=np.int64), kv
     if cfg == "tree":
@@ -415,6 +421,10 @@ def make_config(cfg: str, device="cpu") -> Case:
         return generate(seed=6, q_lens=q_lens, kv_lens=kv_lens, num_heads=32, kv_num_heads=8,
                         head_dim=128, n_q=64, n_kv=8192 + 64, dtype=torch.float16,
                         tree="spec", device=device, name="cfgtree")
+    if cfg == "4p":
+        return generate(seed=4, q_lens=q_lens, kv_lens=kv_lens, num_heads=32, kv_num_heads=8,
+                        head_dim=128, n_q=1, n_kv=32768, dtype=torch.float16, kv_form="paged",
+                        page_size=64, pass_query_lengths=False, device=device, name="cfg4p")
     if cfg in ("4a", "4b"):
         return generate(seed=4, q_lens=q_lens, kv_lens=kv_lens, num_heads=32, kv_num_heads=8,
                         head_dim=128, n_q=1, n_kv=32768, dtype=torch.float16,

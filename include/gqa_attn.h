@@ -46,6 +46,15 @@
  * the drafts on its own ancestor chain, itself included; the rule is ANDed
  * with causal_kind and the mask.
  *
+ * Paged KV (TensorRT Edge-LLM "TensorRT Plugins Guide", AttentionPlugin
+ * decoder tensor contract: kv_page_table [N, 2, max_pages_per_sequence], a
+ * page-table view into resident paged KV pools).  With kv_form
+ * GQA_FORM_PAGED, k and v are pools of pages [P, H_kv, page_size, D] (the
+ * same shape; they may be one tensor), kv_page_table is [B, 2, kv_max_pages]
+ * int32 and key j of sequence b is row j % page_size of page
+ * kv_page_table[b][0][j / page_size] of k, and of page
+ * kv_page_table[b][1][j / page_size] of v.  kv_lengths [B] is required.
+ *
  * Ownership: the caller owns every buffer (all device pointers unless noted);
  * the library never allocates, frees or synchronizes on the forward path
  * and launches asynchronously on the caller's stream.
@@ -69,7 +78,8 @@ typedef enum {
     GQA_DT_BOOL = 4      /* one byte, nonzero = may attend; masks only */
 } gqa_dtype_t;
 
-typedef enum { GQA_FORM_PADDED_BHND = 0, GQA_FORM_PACKED_NHD = 1 } gqa_form_t;
+/* GQA_FORM_PAGED is a KV form only: see "Paged KV" above. */
+typedef enum { GQA_FORM_PADDED_BHND = 0, GQA_FORM_PACKED_NHD = 1, GQA_FORM_PAGED = 2 } gqa_form_t;
 typedef enum {
     GQA_CAUSAL_NONE = 0,
     GQA_CAUSAL_UPPER_LEFT = 1,
@@ -113,6 +123,11 @@ typedef struct {
  * batch: B.  Must equal q.shape[0] / k.shape[0] for padded forms; when both
  *      forms are packed it is the only source of B on the host.
  * out: Y in q's form and shape; dtype of q, except f16 when q is fp8.
+ * kv_page_table, kv_max_pages: paged KV only (device int32 [B, 2,
+ *      kv_max_pages], contiguous).  page_size must be a power of two, >= 32
+ *      for the decode step and >= 64 otherwise; paged KV supports softmax
+ *      without Q/DQ.  Device-side preconditions: kv_len_b <= kv_max_pages *
+ *      page_size and every page index a sequence uses lies in [0, P).
  * tree_parents: optional device int32, token-aligned with q's rows ([T_q]
  *      packed, [B, N_q] contiguous padded); see "Tree decoding" above.
  *      Padded q needs N_q <= 64.  Packed q: a sequence's drafts beyond the
@@ -143,6 +158,8 @@ typedef struct {
     int32_t num_heads;    /* H_q */
     int32_t kv_num_heads; /* H_kv; H_q % H_kv == 0 */
     const int32_t* tree_parents; /* NULL: no tree (ordinary attention) */
+    const int32_t* kv_page_table; /* paged KV: [B, 2, kv_max_pages]; else NULL */
+    int32_t kv_max_pages;
 } gqa_attn_args_t;
 
 /* Check every host-visible property of args; launches nothing, touches no
@@ -173,7 +190,8 @@ const char* gqa_attn_last_error(void);
 int gqa_attn_last_hip_error(void);
 
 /* Library ABI version (bumped on any change of these declarations or of
- * those in gqa_kv_cache.h; 2 adds the KV-cache update, 3 tree_parents). */
+ * those in gqa_kv_cache.h; 2 adds the KV-cache update, 3 tree_parents, 4 paged
+ * KV). */
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

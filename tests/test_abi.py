@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
     assert "gqa_kv_cache_update" in names and "gqa_kv_cache_update_validate" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 3
+    assert lib.gqa_attn_abi_version() == 4
 
 
 _addr = [0x100000]
@@ -227,3 +227,41 @@ def test_tree_parents_validation():
     a = base_args(PACKED, PADDED, nq=100, nkv=120)
     a.tree_parents = 0x7200000
     assert st(a) == capi.GQA_OK, capi.last_error()
+
+
+def _paged_args(nq=1, ps=64, P=40, pages=8, qdq=0):
+    a = base_args(nq=nq)
+    a.kv_form = 2
+    a.k = fake([P, 2, ps, 128], F16)
+    a.v = fake([P, 2, ps, 128], F16)
+    a.kv_lengths = 0x7100000
+    a.kv_page_table = 0x7300000
+    a.kv_max_pages = pages
+    a.qdq = qdq
+    return a
+
+
+def test_paged_kv_validation():
+    assert st(_paged_args(nq=1, ps=32)) == capi.GQA_OK, capi.last_error()      # decode
+    assert st(_paged_args(nq=64, ps=64)) == capi.GQA_OK, capi.last_error()     # prefill
+    assert st(_paged_args(nq=64, ps=32)) == capi.GQA_ERR_UNSUPPORTED           # prefill pages < 64
+    assert st(_paged_args(nq=1, ps=48)) == capi.GQA_ERR_UNSUPPORTED            # not a power of two
+    assert st(_paged_args(nq=1, ps=16)) == capi.GQA_ERR_UNSUPPORTED            # < 32
+    a = _paged_args(nq=64, ps=64, qdq=2)
+    a.qscale = 1 / 64
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED                                   # Q/DQ
+    a = _paged_args()
+    a.kv_page_table = None
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a = _paged_args()
+    a.kv_lengths = None
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a = _paged_args()
+    a.kv_max_pages = 0
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
+    a = base_args()
+    a.kv_page_table = 0x7300000
+    assert st(a) == capi.GQA_ERR_INVALID_ARG                                   # table without paging
+    a = _paged_args()
+    a.kv_form = 3
+    assert st(a) == capi.GQA_ERR_INVALID_ARG
