@@ -81,6 +81,28 @@ struct Decode {
         4 * WAVE_LDS > 4 * MERGE_FLOATS * 4 ? 4 * WAVE_LDS : 4 * MERGE_FLOATS * 4;
     typedef typename Vec8<TQ>::type V8;
     typedef typename std::conditional<KV8, u32x2, u32x4>::type ChunkT;
+    // K operand registers per 16-key block: 16-bit K, one 16-byte chunk (8
+    // values) per k-step; fp8 K, one 16-byte chunk per two k-steps.
+    static constexpr int KCH = KV8 ? D / 64 : D / 32;
+    // Channel of the first of the 8 values lane group g feeds into k-step ks.
+    // The dot product may pair channels with MFMA k-slots in any order, as
+    // long as K and Q use the same one: fp8 K lanes take 16 contiguous bytes
+    // (channels 64 (ks/2) + 16 g .. +15) that serve k-steps ks and ks+1.
+    __device__ __forceinline__ static int kchan(int ks, int g) {
+        return KV8 ? (ks >> 1) * 64 + g * 16 + (ks & 1) * 8 : ks * 32 + g * 8;
+    }
+    // The 8 K values of k-step ks out of the lane's chunks.
+    __device__ __forceinline__ static ChunkT kpart(const u32x4 (&k)[KCH], int ks) {
+        if constexpr (KV8) {
+            const u32x4 c = k[ks >> 1];
+            u32x2 r;
+            r[0] = c[(ks & 1) * 2];
+            r[1] = c[(ks & 1) * 2 + 1];
+            return r;
+        } else {
+            return k[ks];
+        }
+    }
 
     // XOR swizzle of the 16-byte chunks of V row `key` in LDS, chosen so the
     // transpose reads of one instruction (16 keys x 32 bytes for 16-bit V,
@@ -121,7 +143,7 @@ struct Decode {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 V8 a = {};
-                if (ok) a = *(const V8*)(qrow + (ks * 32 + g * 8) * 2);
+                if (ok) a = *(const V8*)(qrow + kchan(ks, g) * 2);
                 qreg[ks] = a;
             }
         }
@@ -147,7 +169,7 @@ struct Decode {
         // V chunks.  Two sets: the next tile is in flight while the current
         // one is computed.
         struct Tile {
-            ChunkT k[2][D / 32];
+            u32x4 k[2][KCH];
             u32x4 v[VINS];
         };
         // Rows [0, k1) of this sequence: keys past the split's end read as
@@ -173,9 +195,9 @@ struct Decode {
                 for (int kb = 0; kb < 2; ++kb) {
                     const int jj = kb * 16 + l16;
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks)
-                        buf_load(kt, (uint32_t)(((int64_t)jj * p.k.sn + ks * 32 + g * 8) * KES),
-                                 t.k[kb][ks]);
+                    for (int kc = 0; kc < KCH; ++kc)
+                        buf_load(kt, (uint32_t)(((int64_t)jj * p.k.sn + kchan(kc * (KV8 ? 2 : 1), g)) * KES),
+                                 t.k[kb][kc]);
                 }
 #pragma unroll
                 for (int i = 0; i < VINS; ++i) {
@@ -188,9 +210,9 @@ struct Decode {
             for (int kb = 0; kb < 2; ++kb) {
                 const int j = j0 + kb * 16 + l16;
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks)
-                    buf_load(krs, (uint32_t)(((int64_t)j * p.k.sn + ks * 32 + g * 8) * KES),
-                             t.k[kb][ks]);
+                for (int kc = 0; kc < KCH; ++kc)
+                    buf_load(krs, (uint32_t)(((int64_t)j * p.k.sn + kchan(kc * (KV8 ? 2 : 1), g)) * KES),
+                             t.k[kb][kc]);
             }
 #pragma unroll
             for (int i = 0; i < VINS; ++i) {
@@ -205,7 +227,7 @@ struct Decode {
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4 acc = {};
 #pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) acc = mfma16(to8(t.k[kb][ks]), qreg[ks], acc);
+                for (int ks = 0; ks < D / 32; ++ks) acc = mfma16(to8(kpart(t.k[kb], ks)), qreg[ks], acc);
                 st[kb] = acc;
             }
             // ---- V tile, row-major, into this wave's LDS (swizzled chunks)
