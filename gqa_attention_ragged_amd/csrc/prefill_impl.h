@@ -67,6 +67,10 @@ struct Cfg {
     // (row stride padded by 16 bytes against bank conflicts).
     static constexpr int MROW = BN * 2 + 16;
     static constexpr int MBYTES = 32 * MROW;
+    // Q rows (input type) and O rows (16-bit output) as 16-byte chunks; one
+    // 1 KiB copy instruction moves QRPI (ORPI) rows, 32 rows take QINS (OINS).
+    static constexpr int QROW = D * ES, QCH = QROW / 16, QRPI = 64 / QCH, QINS = 32 / QRPI;
+    static constexpr int OROW = D * 2, OCH = OROW / 16, ORPI = 64 / OCH, OINS = 32 / ORPI;
 };
 
 // Element e of an 8-element chunk, as raw bits.
@@ -142,6 +146,8 @@ enum Mode { MODE_SOFTMAX = 0, MODE_SOFTMAX_QDQ = 1, MODE_NONE = 2, MODE_SOFTMAX_
 constexpr float kLazyRescale = 8.0f;  // log2 units
 // s_waitcnt immediate: vmcnt(0), expcnt / lgkmcnt not waited on.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate: lgkmcnt(0) (LDS), vmcnt / expcnt not waited on.
+constexpr int kWaitLgkmcnt0 = 0xC07F;
 
 // Mask variants of the general kernel: none; read per lane from global memory
 // (any kind and layout); staged through LDS as 16-bit additive values -- f16
@@ -168,6 +174,14 @@ struct Prefill {
     // of range: zeros, no memory access) into a spare 1 KiB after the stage,
     // so that the copy has no wave-dependent branches.
     static constexpr int SPARE = (C::NKD % 4 || C::NVD % 4) ? 1024 : 0;
+    // Q / O tiles staged through LDS, row-major with XOR-swizzled 16-byte
+    // chunks (chunk c of row r at c ^ (r mod chunks per row)) so that the
+    // 32 rows of an operand read spread over the banks.  Each wave stages
+    // 32 rows: Q in stage 1 (4 x 32 Q rows), O in stages 0 and 1 (2 waves
+    // each).
+    static_assert(4 * 32 * C::QROW <= SSTAGE && 2 * 32 * C::OROW <= SSTAGE, "Q / O staging fits");
+    __device__ __forceinline__ static int q_swz(int row) { return row & (C::QCH - 1); }
+    __device__ __forceinline__ static int o_swz(int row) { return row & (C::OCH - 1); }
     // BMM1 B operand held in registers for the whole kernel: 8 x 16-bit
     // values per k-step, or 32 E4M3FN codes per k-step.
     typedef typename std::conditional<C::FP8, i32x8, V8>::type QOp;
@@ -858,36 +872,50 @@ struct Prefill {
             if constexpr (STAGED) load_mask(p, c, c.t0, rm0);
         }
 
-        // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg)
+        // ---- Q operand (B of S^T = K Q^T): lane (row lr, group lg).  The
+        // wave's 32 rows are copied into its slice of stage 1 (free until the
+        // key loop starts) by loads that write LDS directly, each moving
+        // 1 KiB of whole rows, then read in operand layout.
         QRegs qreg;
         {
-            const bool ok = c.i < c.q_len;
-            const char* qrow = (const char*)p.q.ptr +
-                               (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.i * p.q.sn) * C::ES;
+            char* qs = st1 + wave * 32 * C::QROW;
+            const int nrows = max(0, min(32, c.q_len - c.wr0));
+            const __amdgpu_buffer_rsrc_t qr = make_rsrc(
+                (const char*)p.q.ptr +
+                    (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.wr0 * p.q.sn) * C::ES,
+                rows_bytes(nrows, p.q.sn, D, C::ES));
 #pragma unroll
-            for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                if constexpr (C::FP8) {
-                    u32x4 lo = {}, hi = {};
-                    if (ok) {
-                        const u32x4* src = (const u32x4*)(qrow + ks * 64 + lg * 32);
-                        lo = src[0];
-                        hi = src[1];
-                    }
-                    i32x8 a;
-                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
-                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-                    qreg[ks] = a;
-                } else {
-                    V8 a = {};
-                    if (ok) a = *(const V8*)(qrow + (ks * 16 + lg * 8) * 2);
-                    qreg[ks] = a;
-                }
+            for (int k = 0; k < C::QINS; ++k) {
+                const int row = k * C::QRPI + lane / C::QCH;
+                const int ch = (lane % C::QCH) ^ q_swz(row);  // source chunk of this position
+                buf_load_lds16(qr, qs + k * 1024,
+                               (uint32_t)((int64_t)row * p.q.sn * C::ES + ch * 16));
             }
             // Q (and the first tile) must be resident before the key loop:
             // otherwise the compiler cannot tell the Q loads from the tile
             // copies of the loop and waits for all of them before the first
             // MFMA.
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            const char* qrow = qs + lr * C::QROW;
+#pragma unroll
+            for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                if constexpr (C::FP8) {
+                    // 32 bytes: chunks 4 ks + 2 lg and 4 ks + 2 lg + 1
+                    const int c0 = ks * 4 + lg * 2;
+                    const u32x4 lo = *(const u32x4*)(qrow + ((c0 ^ q_swz(lr)) << 4));
+                    const u32x4 hi = *(const u32x4*)(qrow + (((c0 + 1) ^ q_swz(lr)) << 4));
+                    i32x8 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                    qreg[ks] = a;
+                } else {
+                    // 16 bytes: chunk 2 ks + lg
+                    qreg[ks] = *(const V8*)(qrow + (((ks * 2 + lg) ^ q_swz(lr)) << 4));
+                }
+            }
+            // the operand reads complete before the barrier that lets the
+            // key loop's copies overwrite stage 1
+            __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
         }
 
         ORegs o;
@@ -939,19 +967,32 @@ struct Prefill {
         }
 
         // ---- epilogue: lane (row lr, group lg) holds O^T[d][row] for
-        // d = db*32 + rq*8 + lg*4 + u.
-        if (c.i < c.q_len) {
-            TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)c.i * p.o_sn;
+        // d = db*32 + rq*8 + lg*4 + u.  The wave's 32 output rows go through
+        // its slice of the stages (free after the key loop's last barrier)
+        // so that every store writes 1 KiB of whole rows.
+        {
+            char* os = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * C::OROW;
+            typedef TO TO4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
-                    typedef TO TO4 __attribute__((ext_vector_type(4)));
                     TO4 w;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) w[u] = to_t(o[db][rq * 4 + u] * factor, (TO*)nullptr);
-                    *(TO4*)(orow + db * 32 + rq * 8 + lg * 4) = w;
+                    const int ch = (db * 4 + rq) ^ o_swz(lr);
+                    *(TO4*)(os + lr * C::OROW + ch * 16 + lg * 8) = w;
                 }
+            const int nrows = min(32, c.q_len - c.wr0);
+            char* obase = (char*)p.out +
+                          (o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)c.wr0 * p.o_sn) * 2;
+#pragma unroll
+            for (int k = 0; k < C::OINS; ++k) {
+                const int row = k * C::ORPI + lane / C::OCH;
+                const int ch = lane % C::OCH;
+                const u32x4 w = *(const u32x4*)(os + row * C::OROW + ((ch ^ o_swz(row)) << 4));
+                if (row < nrows) *(u32x4*)(obase + (int64_t)row * p.o_sn * 2 + ch * 16) = w;
+            }
         }
     }
 };
