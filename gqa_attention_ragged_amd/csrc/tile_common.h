@@ -61,23 +61,39 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
     if (wave == 0) {
         if (lane == 0) s_map[0] = -1;
         if (p.batch <= 64) {
-            const int b = lane;
-            const int n = b < p.batch ? (q_len_of(p, b) + R - 1) / R : 0;
-            const int key = b < p.batch ? kv_len_of(p, b) : -1;
-            // rank of b in the dispatch order, then the row tiles ahead of it
-            int rank = 0;
-            for (int j = 0; j < p.batch; ++j) {
-                const int kj = __builtin_amdgcn_readlane(key, j);
-                rank += (kj > key) || (kj == key && j < b);
+            // Bitonic sort of the (KV length, index) pairs across the 64
+            // lanes into dispatch order (longer first, then lower index;
+            // lanes past the batch sort last), then an inclusive scan of the
+            // row-tile counts in that order.
+            int key = lane < p.batch ? kv_len_of(p, lane) : -1;
+            int idx = lane;
+            int n = lane < p.batch ? (q_len_of(p, lane) + R - 1) / R : 0;  // row tiles
+#pragma unroll
+            for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    const int pk = __shfl_xor(key, stride), pi = __shfl_xor(idx, stride);
+                    const int pn = __shfl_xor(n, stride);
+                    // does the partner's pair come first in dispatch order?
+                    const bool pfirst = pk > key || (pk == key && pi < idx);
+                    const bool lower = (lane & stride) == 0;
+                    const bool fwd = size == 64 || (lane & size) == 0;  // run direction
+                    if (pfirst == (lower == fwd)) {
+                        key = pk;
+                        idx = pi;
+                        n = pn;
+                    }
+                }
             }
-            int ahead = 0;
-            for (int j = 0; j < p.batch; ++j) {
-                const int nj = __builtin_amdgcn_readlane(n, j);
-                const int rj = __builtin_amdgcn_readlane(rank, j);
-                ahead += rj < rank ? nj : 0;
+            int incl = n;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
             }
-            if (n > 0 && pos >= ahead && pos < ahead + n) {
-                s_map[0] = b;
+            const int ahead = incl - n;
+            if (n > 0 && pos >= ahead && pos < incl) {
+                s_map[0] = idx;
                 s_map[1] = n - 1 - (pos - ahead);
             }
         } else {
