@@ -120,6 +120,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_pair(float a, float b) {
 __device__ __forceinline__ uint32_t f32_to_e4m3_pair_unsat(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
 }
+// Four fp32 values -> one dword of E4M3FN codes (a, b, c, d in bytes 0..3),
+// round to nearest even; SAT clamps to +-448 first (see above).  The second
+// conversion writes the high half-word and keeps the low one.
+template <bool SAT>
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+    if (SAT) {
+        a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+        b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+        c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+        d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+    }
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
 template <int BYTE>
 __device__ __forceinline__ float e4m3_to_f32(uint32_t word) {
     return __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);

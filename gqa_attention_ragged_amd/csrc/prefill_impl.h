@@ -595,9 +595,8 @@ struct Prefill {
 #pragma unroll
                             for (int w = 0; w < 8; ++w) {
                                 const int kb = w >> 2, r0 = (w & 3) * 4;
-                                uint32_t lo = f32_to_e4m3_pair(s[kb][r0], s[kb][r0 + 1]);
-                                uint32_t hi = f32_to_e4m3_pair(s[kb][r0 + 2], s[kb][r0 + 3]);
-                                codes[w] = (int)(lo | (hi << 16));
+                                codes[w] = (int)f32x4_to_e4m3<true>(s[kb][r0], s[kb][r0 + 1],
+                                                                    s[kb][r0 + 2], s[kb][r0 + 3]);
                             }
                             bmm2_fp8(stage + C::KBYTES, codes, o);
                         } else {
@@ -679,9 +678,7 @@ struct Prefill {
                                 float x1 = fast_exp2(__builtin_fmaf(s[kb][r0 + 1], eff, -m_q));
                                 float x2 = fast_exp2(__builtin_fmaf(s[kb][r0 + 2], eff, -m_q));
                                 float x3 = fast_exp2(__builtin_fmaf(s[kb][r0 + 3], eff, -m_q));
-                                uint32_t lo = SAT ? f32_to_e4m3_pair(x0, x1) : f32_to_e4m3_pair_unsat(x0, x1);
-                                uint32_t hi = SAT ? f32_to_e4m3_pair(x2, x3) : f32_to_e4m3_pair_unsat(x2, x3);
-                                codes[w] = (int)(lo | (hi << 16));
+                                codes[w] = (int)f32x4_to_e4m3<SAT>(x0, x1, x2, x3);
                             }
                             bmm2_fp8(stage + C::KBYTES, codes, o);
                         } else {
