@@ -360,11 +360,16 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // Splitting only pays while the workgroups cannot fill the GPU once: the
     // fp32 partials cost rows * H_q * S * (D + 2) * 4 bytes written and read
     // again (measured on the chunked-context workload, 576 workgroups: no
-    // split 449 TFLOP/s, 6 slices 358).
-    if (a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF && qdt != GQA_DT_FP8_E4M3 &&
-        wgs < slots && kv_tiles >= 8) {
-        int64_t S = (2 * slots + wgs - 1) / wgs;
-        S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
+    // split 508 TFLOP/s, 2 slices 488, 4 slices 460; tree decoding, 512
+    // workgroups: no split 680, 2 slices 619).
+    const bool can_split = a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
+                           qdt != GQA_DT_FP8_E4M3 && kv_tiles >= 8;
+    if (can_split) {
+        int64_t S = 1;
+        if (wgs < slots) {
+            S = (2 * slots + wgs - 1) / wgs;
+            S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
+        }
         // GQA_ATTN_PREFILL_SPLITS (1..32) overrides the slice count for tuning
         if (const char* e = std::getenv("GQA_ATTN_PREFILL_SPLITS")) {
             const int v = std::atoi(e);
