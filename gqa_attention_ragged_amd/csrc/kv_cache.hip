@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kKvThreads) void kv_copy_kernel(KvUpdateParams p) {
 }
 
 // Sequence of packed update row r: the b with ul[b] <= r < ul[b+1]
-// (binary search over the cumulative lengths).
+// (binary search over the cumulative lengths, here in LDS).
 __device__ __forceinline__ int seq_of_row(const int32_t* ul, int B, int64_t r) {
     int lo = 0, hi = B;  // invariant: ul[lo] <= r < ul[hi]
     while (hi - lo > 1) {
@@ -47,29 +47,45 @@ __device__ __forceinline__ int seq_of_row(const int32_t* ul, int B, int64_t r) {
     return lo;
 }
 
+// Cumulative update lengths cached per workgroup (packed updates of up to
+// kKvLdsSeqs sequences; more read them from global memory).
+constexpr int kKvLdsSeqs = 2048;
+
+// IDX: index type of the unit arithmetic (32-bit when every unit index
+// fits, which turns the per-unit divisions into 32-bit ones).
+template <typename IDX>
 __global__ __launch_bounds__(kKvThreads) void kv_scatter_kernel(KvUpdateParams p) {
-    const int upr = p.row_bytes / 16;
-    const int64_t rows = p.packed ? p.T * p.H : (int64_t)p.B * p.H * p.n_u;
-    const int64_t total = rows * upr;
-    const int64_t stride = (int64_t)gridDim.x * kKvThreads;
-    const int64_t last = p.packed ? (int64_t)p.ul[p.B] : 0;
-    for (int64_t u = (int64_t)blockIdx.x * kKvThreads + threadIdx.x; u < total; u += stride) {
-        const int64_t row = u / upr;
+    __shared__ int32_t s_ul[kKvLdsSeqs + 1];
+    const IDX upr = (IDX)(p.row_bytes / 16);
+    const IDX H = (IDX)p.H;
+    const IDX rows = p.packed ? (IDX)(p.T * p.H) : (IDX)((int64_t)p.B * p.H * p.n_u);
+    const IDX total = rows * upr;
+    const IDX stride = (IDX)gridDim.x * kKvThreads;
+    const int32_t* ul = p.ul;
+    if (p.packed && p.B <= kKvLdsSeqs) {
+        for (int i = threadIdx.x; i <= p.B; i += kKvThreads) s_ul[i] = p.ul[i];
+        __syncthreads();
+        ul = s_ul;
+    }
+    const int64_t last = p.packed ? (int64_t)ul[p.B] : 0;
+    for (IDX u = (IDX)blockIdx.x * kKvThreads + threadIdx.x; u < total; u += stride) {
+        const IDX row = u / upr;
         const int c = (int)(u - row * upr);
         int b, h, t;
         const char* src;
         if (p.packed) {
-            const int64_t r = row / p.H;
-            h = (int)(row - r * p.H);
-            if (r >= last) continue;  // beyond the last sequence's rows
-            b = seq_of_row(p.ul, p.B, r);
-            t = (int)(r - p.ul[b]);
-            src = p.upd + (r * p.u_sn + (int64_t)h * p.u_sh) * p.es;
+            const IDX r = row / H;
+            h = (int)(row - r * H);
+            if ((int64_t)r >= last) continue;  // beyond the last sequence's rows
+            b = seq_of_row(ul, p.B, (int64_t)r);
+            t = (int)((int64_t)r - ul[b]);
+            src = p.upd + ((int64_t)r * p.u_sn + (int64_t)h * p.u_sh) * p.es;
         } else {
-            t = (int)(row % p.n_u);
-            const int64_t bh = row / p.n_u;
-            h = (int)(bh % p.H);
-            b = (int)(bh / p.H);
+            const IDX nu = (IDX)p.n_u;
+            const IDX bh = row / nu;
+            t = (int)(row - bh * nu);
+            b = (int)(bh / H);
+            h = (int)(bh - (IDX)b * H);
             if (p.ul && t >= p.ul[b + 1] - p.ul[b]) continue;
             src = p.upd + ((int64_t)b * p.u_sb + (int64_t)h * p.u_sh + (int64_t)t * p.u_sn) * p.es;
         }
@@ -95,8 +111,12 @@ hipError_t launch_kv_update(const KvUpdateParams& p, hipStream_t stream) {
     }
     const int64_t rows = p.packed ? p.T * p.H : (int64_t)p.B * p.H * p.n_u;
     if (rows > 0 && p.B > 0) {
-        hipLaunchKernelGGL(kv_scatter_kernel, dim3(grid_for(rows * upr)), dim3(kKvThreads), 0,
-                           stream, p);
+        if (rows * upr < ((int64_t)1 << 31) - (int64_t)65536 * kKvThreads)
+            hipLaunchKernelGGL(kv_scatter_kernel<uint32_t>, dim3(grid_for(rows * upr)),
+                               dim3(kKvThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(kv_scatter_kernel<int64_t>, dim3(grid_for(rows * upr)),
+                               dim3(kKvThreads), 0, stream, p);
     }
     return hipGetLastError();
 }
