@@ -788,8 +788,16 @@ struct Prefill {
         kv_end = max(kv_end, 0);
         c.t0 = 0;
         c.t1 = (kv_end + C::BN - 1) / C::BN;
-        if (p.n_splits > 1) {  // split-KV: this workgroup takes one slice of the keys
+        // split-KV: this workgroup takes one slice of the keys.  Slices
+        // cover fixed key ranges: a row tile whose keys fit in one slice is
+        // computed whole by slice 0 and written as final output; the others
+        // write fp32 partials for the combine kernel.  Slices past the keys
+        // of this row tile have nothing to do.
+        int nsl = 1;
+        if (p.n_splits > 1) {
             const int per = p.split_keys / C::BN;
+            nsl = (c.t1 + per - 1) / per;
+            if (bz >= max(nsl, 1)) return;
             c.t0 = min(bz * per, c.t1);
             c.t1 = min(c.t0 + per, c.t1);
         }
@@ -937,7 +945,7 @@ struct Prefill {
         } else {
             sweep<PASS_ONLINE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
             const float l_tot = halves_sum(l_run);
-            if (p.n_splits > 1) {
+            if (nsl > 1) {
                 // split-KV: unnormalized O with its reference max and sum
                 // (exp2 domain); the combine kernel merges the slices.
                 if (c.i < c.q_len) {
@@ -1022,13 +1030,24 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
     const int h = blockIdx.y;
     const int q_len = q_len_of(p, b);
     const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
-    const int S = p.n_splits;
+    // slices with work for this row tile, as the attention kernel counts
+    // them; one slice: the attention kernel wrote the final rows itself
+    const int kv_len = kv_len_of(p, b);
+    int kv_end = kv_len;
+    if (p.causal) {
+        const int diag = p.causal == 1 ? 0 : kv_len - q_len;
+        kv_end = min(kv_end, min(row0 + R, q_len) - 1 + diag + 1);
+    }
+    const int per = p.split_keys / 64;
+    const int S = (max(kv_end, 0) + 64 * per - 1) / (64 * per);
+    if (S <= 1) return;
+    const int SS = p.n_splits;  // slot stride
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t rbase = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
     for (int r = wave; r < R; r += 4) {
         const int i = row0 + r;
         if (i >= q_len) break;
-        const int64_t slot0 = ((rbase + i) * p.hq + h) * S;
+        const int64_t slot0 = ((rbase + i) * p.hq + h) * SS;
         const float m = lane < S ? p.part_ml[(slot0 + lane) * 2] : -INFINITY;
         const float l = lane < S ? p.part_ml[(slot0 + lane) * 2 + 1] : 0.f;
         float M = m;
