@@ -364,13 +364,6 @@ struct Prefill {
         }
     }
 
-    // Whether every (row, key) of this tile is allowed, so the raw scores can
-    // be used as they are (softmax folds the scale into its exp2 argument).
-    __device__ __forceinline__ static bool tile_is_full(const AttnParams& p, const Ctx& c, int tile,
-                                                        float sc) {
-        const int j0 = tile * C::BN;
-        return !HAS_MASK && cl_full(p, c, tile) && sc > 0.f;
-    }
     // Whether the tile is fully allowed by the lengths and the causal rule
     // (the mask aside) for every row of this wave.
     __device__ __forceinline__ static bool cl_full(const AttnParams& p, const Ctx& c, int tile) {
@@ -551,6 +544,8 @@ struct Prefill {
     // the rounding limit (P <= 1), and the clamp is left out.
     // PRIMED: the copy of the first tile into st0 was started by the caller
     // (with the mask tile's registers in rm0).
+    // The score scale sc is positive: the caller moves a non-positive scale
+    // onto Q.
     template <int KIND, bool SAT = true, bool PRIMED = false>
     __device__ __forceinline__ static void sweep(const AttnParams& p, const Ctx& c,
                                                  char* __restrict__ st0, char* __restrict__ st1,
@@ -559,6 +554,7 @@ struct Prefill {
                                                  const u32x4& rm0 = u32x4{}) {
         const bool with_v = KIND != PASS_STATS;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const float kadd = ac / sc;  // staged mask weight on raw scores
         u32x4 rm = {};
         const bool mlds = STAGED;
         if (c.t0 < c.t1) {
@@ -611,18 +607,16 @@ struct Prefill {
                     // into the exp2 argument (fma); otherwise the predicate
                     // scales them and marks disallowed keys with -inf.
                     float eff = sc;
-                    if (STAGED && sc > 0.f) {
+                    if constexpr (STAGED) {
                         // staged mask on raw scores, lengths / causal only
                         // where the tile is not fully allowed
-                        apply_mask_raw(s, stage, ac / sc);
+                        apply_mask_raw(s, stage, kadd);
                         if (!cl_full(p, c, it)) predicate_raw(c, it, s);
-                    } else if (!tile_is_full(p, c, it, sc)) {
-                        if (!HAS_MASK && sc > 0.f) {
-                            predicate_raw(c, it, s);
-                        } else {
-                            predicate(p, c, it, s, sc, ac, false, stage);
-                            eff = 1.f;
-                        }
+                    } else if constexpr (HAS_MASK) {
+                        predicate(p, c, it, s, sc, ac, false, stage);
+                        eff = 1.f;
+                    } else {
+                        if (!cl_full(p, c, it)) predicate_raw(c, it, s);
                     }
                     // row max over the lane's 32 scores: four independent chains
                     float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -928,8 +922,35 @@ struct Prefill {
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
         float m_run = -INFINITY, l_run = 0.f;
         const bool none_norm = MODE == MODE_NONE;
-        const float sc = none_norm ? p.scale * p.k_descale : p.scale * p.k_descale * kLog2e;
+        float sc = none_norm ? p.scale * p.k_descale : p.scale * p.k_descale * kLog2e;
         const float ac = none_norm ? 1.f : kLog2e;
+        // The softmax sweeps keep raw dot products and fold the scale into
+        // the exp2 argument, which needs a positive scale.  A negative scale
+        // moves onto Q (sign bits flipped: every dot product changes sign
+        // exactly); a zero scale zeroes Q and takes scale 1 (all scores 0).
+        if (sc <= 0.f) {
+            const bool neg = sc < 0.f;
+            const uint32_t flip = C::FP8 ? 0x80808080u : 0x80008000u;
+#pragma unroll
+            for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                if constexpr (C::FP8) {
+#pragma unroll
+                    for (int w = 0; w < 8; ++w) {
+                        const uint32_t x = (uint32_t)qreg[ks][w];
+                        qreg[ks][w] = neg ? (int)(x ^ flip) : 0;
+                    }
+                } else {
+                    u32x4 u = __builtin_bit_cast(u32x4, qreg[ks]);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const uint32_t x = u[w];
+                        u[w] = neg ? x ^ flip : 0u;
+                    }
+                    qreg[ks] = __builtin_bit_cast(V8, u);
+                }
+            }
+            sc = neg ? -sc : 1.f;
+        }
         float factor = p.v_descale;
 
         if constexpr (MODE == MODE_NONE) {

@@ -27,7 +27,7 @@ def _lens(rng, B, lo, hi):
 
 def _case(seed, *, qf, kf, causal="none", mask=None, dtype=torch.float16, D=128, hq=8, hkv=2,
           norm="softmax", qdq=None, B=3, qmax=150, kvmax=170, zero=False, n_q_pad=None,
-          kv_fp8=False, mask_heads=1, qscale=None):
+          kv_fp8=False, mask_heads=1, qscale=None, scale=None):
     rng = np.random.default_rng(seed)
     ql = _lens(rng, B, 0 if zero else 1, qmax)
     kl = _lens(rng, B, 0 if zero else 1, kvmax)
@@ -44,7 +44,7 @@ def _case(seed, *, qf, kf, causal="none", mask=None, dtype=torch.float16, D=128,
         query_form=qf, kv_form=kf, dtype=dtype, n_q=n_q, n_kv=int(kl.max()) + 7, q_slack=3,
         kv_slack=2, pass_query_lengths=pass_ql, mask_kind=mask, mask_heads=mask_heads,
         mask_p=0.2, mask_value=-4.0 if seed % 3 else -float("inf"), mask_diag_true=True,
-        causal_kind=causal, norm=norm, qdq=qdq,
+        causal_kind=causal, norm=norm, qdq=qdq, scale=scale,
         qscale=qscale if qscale is not None else (
             float(np.float32(1 / 448.0)) if qdq == "fp8" else 1 / 64.0),
         kv_fp8_from=torch.float16 if kv_fp8 else None,
@@ -108,6 +108,33 @@ def test_head_broadcast_masks_ragged_tails(mask, causal, row_bcast):
     if row_bcast:
         c = dataclasses.replace(c, mask=c.mask[:, :, :1, :].contiguous())
     parity.compare(c, parity.run_gpu(c))
+
+@pytest.mark.parametrize("scale", [-0.0883, 0.0])
+@pytest.mark.parametrize("kind", ["plain", "staged_bool", "f32_mask", "none", "fp8_qdq"])
+def test_non_positive_scale(scale, kind):
+    # A negative or zero score scale: the scores change sign or all become 0
+    # (softmax then spreads evenly over the allowed keys).
+    seed = 470 + ["plain", "staged_bool", "f32_mask", "none", "fp8_qdq"].index(kind) * 2 + (
+        scale == 0.0)
+    if kind == "staged_bool":
+        ql = np.array([31, 1, 70, 33, 17])
+        kl = np.array([101, 40, 333, 77, 9])
+        c = synth.generate(seed=seed, q_lens=ql, kv_lens=np.maximum(kl, ql), num_heads=8,
+                           kv_num_heads=2, head_dim=128, query_form="packed_nhd",
+                           kv_form="padded_bhnd", n_kv=640, q_slack=2, kv_slack=0,
+                           dtype=torch.float16, mask_kind="bool", mask_p=0.2,
+                           mask_diag_true=True, causal_kind="lower_right", scale=scale,
+                           device=DEV, name=f"scale{scale}-staged")
+    elif kind == "fp8_qdq":
+        c = _case(seed, qf="padded_bhnd", kf="padded_bhnd", causal="upper_left", mask="bool",
+                  dtype=torch.float8_e4m3fn, qdq="fp8", qmax=120, kvmax=140, scale=scale)
+    else:
+        c = _case(seed, qf="packed_nhd", kf="packed_nhd",
+                  causal="none" if kind == "none" else "lower_right",
+                  mask="f32" if kind == "f32_mask" else None,
+                  norm="none" if kind == "none" else "softmax", scale=scale)
+    parity.compare(c, parity.run_gpu(c))
+
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", [(4, 4), (8, 4), (8, 2), (8, 1), (12, 4), (6, 2)])
