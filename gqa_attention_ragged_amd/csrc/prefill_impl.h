@@ -702,7 +702,7 @@ struct Prefill {
     template <int MODE>
     __device__ __forceinline__ static void run(const AttnParams& p, char* __restrict__ st0,
                                                char* __restrict__ st1) {
-        __shared__ int s_map[2];
+        __shared__ int s_map[6];
         const int tid = threadIdx.x, lane = tid & 63;
         // wave index in a scalar register: everything derived from it is
         // wave-uniform, and branches on it are scalar branches
@@ -734,8 +734,10 @@ struct Prefill {
 
         Ctx c;
         c.b = b;
-        c.q_len = q_len_of(p, b);
-        c.kv_len = kv_len_of(p, b);
+        c.q_len = __builtin_amdgcn_readfirstlane(s_map[2]);
+        c.kv_len = __builtin_amdgcn_readfirstlane(s_map[3]);
+        const int q_start = __builtin_amdgcn_readfirstlane(s_map[4]);
+        const int kv_start = __builtin_amdgcn_readfirstlane(s_map[5]);
         c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
         c.causal = p.causal != 0;
         c.tree = TREE && p.tree != nullptr;
@@ -753,7 +755,7 @@ struct Prefill {
             // jumping, lane l = draft l: A_l starts as {l} and J_l as its
             // parent; each round A_l |= A_{J_l}, J_l = J_{J_l} doubles the
             // chain length covered, so 6 rounds cover any chain of 64.
-            const int64_t prow = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
+            const int64_t prow = p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q;
             int par = lane < c.q_len ? p.tree[prow + lane] : -1;
             int jmp = (par >= 0 && par < lane) ? par : -1;
             uint32_t a_lo = lane < c.q_len && lane < 32 ? 1u << lane : 0u;
@@ -799,7 +801,10 @@ struct Prefill {
         c.wave_kv_end = c.kv_len;
         if (p.causal) c.wave_kv_end = min(c.wave_kv_end, wave_last + c.diag + 1);
         // paged KV: the head's offset inside a page (the page comes per tile)
-        const int64_t kro = PAGED ? 0 : kv_rowbase(p, p.k, b), vro = PAGED ? 0 : kv_rowbase(p, p.v, b);
+        const int64_t kro = PAGED ? 0
+                            : p.kv_packed ? (int64_t)kv_start * p.k.sn : (int64_t)b * p.k.sb;
+        const int64_t vro = PAGED ? 0
+                            : p.kv_packed ? (int64_t)kv_start * p.v.sn : (int64_t)b * p.v.sb;
         c.kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * C::ES;
         c.vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * C::ES;
         c.kbytes = rows_bytes(c.kv_len, p.k.sn, D, C::ES);
@@ -881,7 +886,8 @@ struct Prefill {
             const int nrows = max(0, min(32, c.q_len - c.wr0));
             const __amdgpu_buffer_rsrc_t qr = make_rsrc(
                 (const char*)p.q.ptr +
-                    (q_rowbase(p, b) + (int64_t)h * p.q.sh + (int64_t)c.wr0 * p.q.sn) * C::ES,
+                    ((p.q_packed ? (int64_t)q_start * p.q.sn : (int64_t)b * p.q.sb) +
+                     (int64_t)h * p.q.sh + (int64_t)c.wr0 * p.q.sn) * C::ES,
                 rows_bytes(nrows, p.q.sn, D, C::ES));
 #pragma unroll
             for (int k = 0; k < C::QINS; ++k) {
@@ -970,7 +976,7 @@ struct Prefill {
                 // split-KV: unnormalized O with its reference max and sum
                 // (exp2 domain); the combine kernel merges the slices.
                 if (c.i < c.q_len) {
-                    const int64_t row = (p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q) + c.i;
+                    const int64_t row = (p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q) + c.i;
                     const int64_t slot = (row * p.hq + h) * p.n_splits + bz;
                     float* po = p.part_o + slot * D;
 #pragma unroll
@@ -1011,7 +1017,8 @@ struct Prefill {
                 }
             const int nrows = min(32, c.q_len - c.wr0);
             char* obase = (char*)p.out +
-                          (o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)c.wr0 * p.o_sn) * 2;
+                          ((p.q_packed ? (int64_t)q_start * p.o_sn : (int64_t)b * p.o_sb) +
+                           (int64_t)h * p.o_sh + (int64_t)c.wr0 * p.o_sn) * 2;
 #pragma unroll
             for (int k = 0; k < C::OINS; ++k) {
                 const int row = k * C::ORPI + lane / C::OCH;
@@ -1043,17 +1050,17 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
     // One wave per (row, head) at a time: lane s holds slice s's (m, l)
     // (S <= 64), the wave reduces M and L, then each lane sums its d values
     // over the slices with the weights broadcast from their lanes.
-    __shared__ int s_map[2];
+    __shared__ int s_map[6];
     const int R = p.rows_per_wg;
     map_tile(p, blockIdx.x, R, s_map);
     const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
     if (b < 0) return;
     const int h = blockIdx.y;
-    const int q_len = q_len_of(p, b);
+    const int q_len = __builtin_amdgcn_readfirstlane(s_map[2]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
     // slices with work for this row tile, as the attention kernel counts
     // them; one slice: the attention kernel wrote the final rows itself
-    const int kv_len = kv_len_of(p, b);
+    const int kv_len = __builtin_amdgcn_readfirstlane(s_map[3]);
     int kv_end = kv_len;
     if (p.causal) {
         const int diag = p.causal == 1 ? 0 : kv_len - q_len;
@@ -1064,7 +1071,8 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
     if (S <= 1) return;
     const int SS = p.n_splits;  // slot stride
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t rbase = p.q_packed ? (int64_t)p.ql[b] : (int64_t)b * p.n_q;
+    const int q_start = __builtin_amdgcn_readfirstlane(s_map[4]);
+    const int64_t rbase = p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q;
     for (int r = wave; r < R; r += 4) {
         const int i = row0 + r;
         if (i >= q_len) break;
@@ -1080,7 +1088,8 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
         const float inv = L > 0.f ? p.v_descale / L : 0.f;
-        TO* orow = (TO*)p.out + o_rowbase(p, b) + (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
+        TO* orow = (TO*)p.out + (p.q_packed ? (int64_t)q_start * p.o_sn : (int64_t)b * p.o_sb) +
+                   (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
         for (int d = lane; d < D; d += 64) {
             float acc = 0.f;
             for (int sp = 0; sp < S; ++sp) {

@@ -4,6 +4,8 @@
 #pragma once
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace gqa {
 
 // V is staged row-major; the 16-byte units of row `key` are XOR-swizzled so
@@ -48,14 +50,67 @@ __device__ __forceinline__ u32x2 tr8(const char* p) {
 }
 
 // ------------------------------------------------------------------ tile map
+// What a workgroup needs of its sequence: lengths and first rows in packed
+// tensors (0 where the tensor is padded).
+struct SeqInfo {
+    int q_len, kv_len, q_start, kv_start;
+};
+__device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int b) {
+    SeqInfo s;
+    s.q_start = p.ql ? p.ql[b] : 0;
+    s.q_len = p.ql ? p.ql[b + 1] - s.q_start : p.n_q;
+    if (p.kv_packed) {
+        s.kv_start = p.kl[b];
+        s.kv_len = p.kl[b + 1] - s.kv_start;
+    } else {
+        s.kv_start = 0;
+        s.kv_len = p.kl ? p.kl[b] : p.n_kv;
+    }
+    return s;
+}
+
+// Lane l receives v of lane l ^ M.  Inside a 16-lane row the exchange is a
+// DPP move (quad permutations, the half-row mirror, the row rotation by 8),
+// with no round trip through LDS; across rows it is a bpermute.
+template <int M>
+__device__ __forceinline__ int xor_lanes(int v) {
+    if constexpr (M == 1) {
+        return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (M == 2) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (M == 4) {
+        // half-row mirror (l ^ 7), then quad reversal (l ^ 3)
+        const int m = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);
+        return __builtin_amdgcn_update_dpp(0, m, 0x1B, 0xF, 0xF, false);
+    } else if constexpr (M == 8) {
+        return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    } else {
+        return __shfl_xor(v, M);
+    }
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// row (lanes without a source add 0), then each row adds the totals of the
+// rows before it through the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Dispatch position `pos` -> (b, row tile within b); sequence b has
 // ceil(q_len_b / R) row tiles.  Positions run over the sequences by
 // decreasing KV length (ties: lower index first; more than 64 sequences:
 // index order), and within a sequence from its last row tile to its first,
 // so the heaviest work items (long rows of long sequences under causal
 // masking) start first and the lightest ones fill the tail.  Wave 0
-// computes the map; the result lands in s_map[0..1] (b = -1 past the last
-// tile).  Block-wide barrier included.
+// computes the map; s_map[0..5] receives b (-1 past the last tile), the
+// row tile, and b's q_len, kv_len, q_start and kv_start, so that the
+// workgroup reads its sequence's lengths from LDS rather than from memory
+// again.  Block-wide barrier included.
 __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, int* s_map) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (wave == 0) {
@@ -65,43 +120,70 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
             // lanes into dispatch order (longer first, then lower index;
             // lanes past the batch sort last), then an inclusive scan of the
             // row-tile counts in that order.
-            int key = lane < p.batch ? kv_len_of(p, lane) : -1;
+            const SeqInfo si = lane < p.batch ? seq_info(p, lane) : SeqInfo{0, -1, 0, 0};
+            int key = si.kv_len;
             int idx = lane;
-            int n = lane < p.batch ? (q_len_of(p, lane) + R - 1) / R : 0;  // row tiles
-#pragma unroll
-            for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-                for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                    const int pk = __shfl_xor(key, stride), pi = __shfl_xor(idx, stride);
-                    const int pn = __shfl_xor(n, stride);
-                    // does the partner's pair come first in dispatch order?
-                    const bool pfirst = pk > key || (pk == key && pi < idx);
-                    const bool lower = (lane & stride) == 0;
-                    const bool fwd = size == 64 || (lane & size) == 0;  // run direction
-                    if (pfirst == (lower == fwd)) {
-                        key = pk;
-                        idx = pi;
-                        n = pn;
-                    }
+            int n = lane < p.batch ? (si.q_len + R - 1) / R : 0;  // row tiles
+            // one compare-exchange step with the partner lane ^ STRIDE
+            auto step = [&](auto stride_c, int size) {
+                constexpr int stride = decltype(stride_c)::value;
+                const int pk = xor_lanes<stride>(key), pi = xor_lanes<stride>(idx);
+                const int pn = xor_lanes<stride>(n);
+                // does the partner's pair come first in dispatch order?
+                const bool pfirst = pk > key || (pk == key && pi < idx);
+                const bool lower = (lane & stride) == 0;
+                const bool fwd = size == 64 || (lane & size) == 0;  // run direction
+                if (pfirst == (lower == fwd)) {
+                    key = pk;
+                    idx = pi;
+                    n = pn;
                 }
-            }
-            int incl = n;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
-            }
+            };
+            using S1 = std::integral_constant<int, 1>;
+            using S2 = std::integral_constant<int, 2>;
+            using S4 = std::integral_constant<int, 4>;
+            using S8 = std::integral_constant<int, 8>;
+            using S16 = std::integral_constant<int, 16>;
+            using S32 = std::integral_constant<int, 32>;
+            step(S1{}, 2);
+            step(S2{}, 4), step(S1{}, 4);
+            step(S4{}, 8), step(S2{}, 8), step(S1{}, 8);
+            step(S8{}, 16), step(S4{}, 16), step(S2{}, 16), step(S1{}, 16);
+            step(S16{}, 32), step(S8{}, 32), step(S4{}, 32), step(S2{}, 32), step(S1{}, 32);
+            step(S32{}, 64), step(S16{}, 64), step(S8{}, 64), step(S4{}, 64), step(S2{}, 64);
+            step(S1{}, 64);
+            const int incl = wave_incl_scan(n);
             const int ahead = incl - n;
-            if (n > 0 && pos >= ahead && pos < incl) {
-                s_map[0] = idx;
-                s_map[1] = n - 1 - (pos - ahead);
+            const uint64_t hit = __ballot(n > 0 && pos >= ahead && pos < incl);
+            if (hit != 0 && __builtin_amdgcn_readlane(idx, (int)__builtin_ctzll(hit)) < p.batch) {
+                // the one matching lane (wave-uniform), then its sequence's
+                // values from the lane that loaded them
+                const int src = (int)__builtin_ctzll(hit);
+                const int b = __builtin_amdgcn_readlane(idx, src);
+                const int t = __builtin_amdgcn_readlane(n - 1 - (pos - ahead), src);
+                const int ql = __builtin_amdgcn_readlane(si.q_len, b);
+                const int kl = __builtin_amdgcn_readlane(si.kv_len, b);
+                const int qs = __builtin_amdgcn_readlane(si.q_start, b);
+                const int ks = __builtin_amdgcn_readlane(si.kv_start, b);
+                if (lane == 0) {
+                    s_map[0] = b;
+                    s_map[1] = t;
+                    s_map[2] = ql;
+                    s_map[3] = kl;
+                    s_map[4] = qs;
+                    s_map[5] = ks;
+                }
             }
         } else {
             int acc = 0;
             for (int base = 0; base < p.batch; base += 64) {
                 const int b = base + lane;
                 int n = 0;
-                if (b < p.batch) n = (q_len_of(p, b) + R - 1) / R;
+                SeqInfo si = {0, 0, 0, 0};
+                if (b < p.batch) {
+                    si = seq_info(p, b);
+                    n = (si.q_len + R - 1) / R;
+                }
                 int incl = n;
 #pragma unroll
                 for (int off = 1; off < 64; off <<= 1) {
@@ -112,6 +194,10 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
                 if (n > 0 && pos >= acc + excl && pos < acc + incl) {
                     s_map[0] = b;
                     s_map[1] = n - 1 - (pos - acc - excl);
+                    s_map[2] = si.q_len;
+                    s_map[3] = si.kv_len;
+                    s_map[4] = si.q_start;
+                    s_map[5] = si.kv_start;
                 }
                 acc += __shfl(incl, 63);
                 if (acc > pos) break;
