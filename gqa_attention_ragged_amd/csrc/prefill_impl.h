@@ -709,6 +709,7 @@ struct Prefill {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lr = lane & 31, lg = lane >> 5;
         const int R = p.rows_per_wg;
+        const SeqInfo si = map_lane_info(p);  // loads in flight during the remap
         int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
         if (p.xcds > 1) {
             // Consecutive workgroup ids go to the XCDs in turn (id % xcds),
@@ -725,7 +726,7 @@ struct Prefill {
             by = li / (nx * nz);
         }
         // dispatch position -> (sequence, row tile), heaviest first
-        map_tile(p, bx, R, s_map);
+        map_tile(p, bx, R, s_map, si);
         // (b, row tile) are workgroup-uniform: read them into scalar registers
         // so that every address and buffer descriptor built from them is
         // scalar too (a descriptor in vector registers needs a loop per load).
@@ -1052,7 +1053,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
     // over the slices with the weights broadcast from their lanes.
     __shared__ int s_map[6];
     const int R = p.rows_per_wg;
-    map_tile(p, blockIdx.x, R, s_map);
+    map_tile(p, blockIdx.x, R, s_map, map_lane_info(p));
     const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
     if (b < 0) return;
     const int h = blockIdx.y;

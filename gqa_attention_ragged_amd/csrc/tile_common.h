@@ -101,30 +101,43 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     return x;
 }
 
+// Wave 0's per-lane sequence values for the map below (lane l: sequence l
+// when the batch has at most 64 sequences).  Called at kernel start so that
+// the loads overlap the work before the map.
+__device__ __forceinline__ SeqInfo map_lane_info(const AttnParams& p) {
+    const int lane = threadIdx.x & 63;
+    SeqInfo si = {0, -1, 0, 0};
+    if (threadIdx.x < 64 && p.batch <= 64 && lane < p.batch) si = seq_info(p, lane);
+    return si;
+}
+
 // Dispatch position `pos` -> (b, row tile within b); sequence b has
 // ceil(q_len_b / R) row tiles.  Positions run over the sequences by
 // decreasing KV length (ties: lower index first; more than 64 sequences:
 // index order), and within a sequence from its last row tile to its first,
 // so the heaviest work items (long rows of long sequences under causal
 // masking) start first and the lightest ones fill the tail.  Wave 0
-// computes the map; s_map[0..5] receives b (-1 past the last tile), the
-// row tile, and b's q_len, kv_len, q_start and kv_start, so that the
-// workgroup reads its sequence's lengths from LDS rather than from memory
-// again.  Block-wide barrier included.
-__device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, int* s_map) {
+// computes the map from its lanes' `si` (map_lane_info); s_map[0..5]
+// receives b (-1 past the last tile), the row tile, and b's q_len, kv_len,
+// q_start and kv_start, so that the workgroup reads its sequence's lengths
+// from LDS rather than from memory again.  Block-wide barrier included.
+__device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, int* s_map,
+                                         const SeqInfo& si) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (wave == 0) {
         if (lane == 0) s_map[0] = -1;
         if (p.batch <= 64) {
-            // Bitonic sort of the (KV length, index) pairs across the 64
-            // lanes into dispatch order (longer first, then lower index;
-            // lanes past the batch sort last), then an inclusive scan of the
-            // row-tile counts in that order.
-            const SeqInfo si = lane < p.batch ? seq_info(p, lane) : SeqInfo{0, -1, 0, 0};
+            // Bitonic sort of the (KV length, index) pairs into dispatch
+            // order (longer first, then lower index; lanes past the batch
+            // sort last) over groups of NMAX = 16, 32 or 64 lanes, the
+            // smallest that holds the batch (groups past the first hold
+            // only empty lanes), then an inclusive scan of the row-tile
+            // counts in that order.
             int key = si.kv_len;
             int idx = lane;
             int n = lane < p.batch ? (si.q_len + R - 1) / R : 0;  // row tiles
-            // one compare-exchange step with the partner lane ^ STRIDE
+            const int nmax = p.batch <= 16 ? 16 : p.batch <= 32 ? 32 : 64;
+            // one compare-exchange step with the partner lane ^ stride
             auto step = [&](auto stride_c, int size) {
                 constexpr int stride = decltype(stride_c)::value;
                 const int pk = xor_lanes<stride>(key), pi = xor_lanes<stride>(idx);
@@ -132,7 +145,7 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
                 // does the partner's pair come first in dispatch order?
                 const bool pfirst = pk > key || (pk == key && pi < idx);
                 const bool lower = (lane & stride) == 0;
-                const bool fwd = size == 64 || (lane & size) == 0;  // run direction
+                const bool fwd = size == nmax || (lane & size) == 0;  // run direction
                 if (pfirst == (lower == fwd)) {
                     key = pk;
                     idx = pi;
@@ -149,9 +162,13 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
             step(S2{}, 4), step(S1{}, 4);
             step(S4{}, 8), step(S2{}, 8), step(S1{}, 8);
             step(S8{}, 16), step(S4{}, 16), step(S2{}, 16), step(S1{}, 16);
-            step(S16{}, 32), step(S8{}, 32), step(S4{}, 32), step(S2{}, 32), step(S1{}, 32);
-            step(S32{}, 64), step(S16{}, 64), step(S8{}, 64), step(S4{}, 64), step(S2{}, 64);
-            step(S1{}, 64);
+            if (nmax >= 32) {
+                step(S16{}, 32), step(S8{}, 32), step(S4{}, 32), step(S2{}, 32), step(S1{}, 32);
+            }
+            if (nmax == 64) {
+                step(S32{}, 64), step(S16{}, 64), step(S8{}, 64), step(S4{}, 64), step(S2{}, 64);
+                step(S1{}, 64);
+            }
             const int incl = wave_incl_scan(n);
             const int ahead = incl - n;
             const uint64_t hit = __ballot(n > 0 && pos >= ahead && pos < incl);
