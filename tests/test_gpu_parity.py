@@ -145,6 +145,23 @@ def test_head_groups_and_head_size(D, heads):
     parity.compare(c, parity.run_gpu(c))
 
 
+@pytest.mark.parametrize("B", [13, 20, 32, 40, 64])
+def test_dispatch_map_batch_sizes(B):
+    # The row-tile map sorts the sequences over 16, 32 or 64 lanes depending
+    # on the batch: every size class, with empty sequences and ties in KV
+    # length, each output row written exactly once.
+    rng = np.random.default_rng(4000 + B)
+    ql = rng.integers(0, 70, size=B)
+    kl = rng.choice([0, 1, 40, 96, 97, 150], size=B)
+    kl = np.maximum(kl, ql)
+    c = synth.generate(seed=4000 + B, q_lens=ql, kv_lens=kl, num_heads=8, kv_num_heads=2,
+                       head_dim=64, query_form="packed_nhd",
+                       kv_form="padded_bhnd" if B % 2 else "packed_nhd",
+                       causal_kind="lower_right", q_slack=3, kv_slack=3, device=DEV,
+                       name=f"map-B{B}")
+    parity.compare(c, parity.run_gpu(c))
+
+
 def test_ragged_with_empty_sequences():
     c = synth.generate(seed=401, q_lens=[0, 5, 0, 64, 1, 33], kv_lens=[3, 0, 0, 70, 1, 200],
                        num_heads=8, kv_num_heads=2, head_dim=128, query_form="packed_nhd",
