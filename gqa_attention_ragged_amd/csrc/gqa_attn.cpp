@@ -357,17 +357,19 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     const int64_t kv_tiles = (kv_max + 63) / 64;
     // Concurrent workgroups: two 4-wave workgroups per CU (256 CUs).
     const int64_t slots = 512;
-    // Splitting only pays while the workgroups cannot fill the GPU once: the
-    // fp32 partials cost rows * H_q * S * (D + 2) * 4 bytes written and read
-    // again (measured on the chunked-context workload, 576 workgroups: no
-    // split 508 TFLOP/s, 2 slices 488, 4 slices 460; tree decoding, 512
-    // workgroups: no split 680, 2 slices 619).
+    // Splitting pays while the workgroups fill the GPU about once (the
+    // longest row tile then sets the time); the fp32 partials cost
+    // rows * H_q * S * (D + 2) * 4 bytes written and read again.  Measured
+    // on the chunked-context workload (576 workgroups at most, 496 with
+    // work): no split 510 TFLOP/s, 2 slices 570, 3 slices 591, 4 slices 549;
+    // tree decoding (512 workgroups): no split 662, 2 slices 650, 3 slices
+    // 669.  At most 1.25 rounds of workgroups: slices for about 3 rounds.
     const bool can_split = a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
                            qdt != GQA_DT_FP8_E4M3 && kv_tiles >= 8;
     if (can_split) {
         int64_t S = 1;
-        if (wgs < slots) {
-            S = (2 * slots + wgs - 1) / wgs;
+        if (wgs < slots * 5 / 4) {
+            S = (3 * slots + wgs - 1) / wgs;
             S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
         }
         // GQA_ATTN_PREFILL_SPLITS (1..32) overrides the slice count for tuning

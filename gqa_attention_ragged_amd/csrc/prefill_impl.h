@@ -1048,9 +1048,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
 // (exp2 domain) and writes the valid rows of Y.
 template <typename TO, int D>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
-    // One wave per (row, head) at a time: lane s holds slice s's (m, l)
-    // (S <= 64), the wave reduces M and L, then each lane sums its d values
-    // over the slices with the weights broadcast from their lanes.
+    // CT threads per (row, head), each owning D / CT consecutive values of
+    // d: every thread reads the slices' (m, l), then issues its 16-byte
+    // partial loads of all slices before it needs them, so the reads of a
+    // workgroup are in flight together.
+    constexpr int CT = 8, DPT = D / CT;
     __shared__ int s_map[6];
     const int R = p.rows_per_wg;
     map_tile(p, blockIdx.x, R, s_map, map_lane_info(p));
@@ -1071,35 +1073,39 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
     const int S = (max(kv_end, 0) + 64 * per - 1) / (64 * per);
     if (S <= 1) return;
     const int SS = p.n_splits;  // slot stride
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int q_start = __builtin_amdgcn_readfirstlane(s_map[4]);
     const int64_t rbase = p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q;
-    for (int r = wave; r < R; r += 4) {
+    const int part = threadIdx.x % CT;
+    for (int r = threadIdx.x / CT; r < R; r += 256 / CT) {
         const int i = row0 + r;
         if (i >= q_len) break;
         const int64_t slot0 = ((rbase + i) * p.hq + h) * SS;
-        const float m = lane < S ? p.part_ml[(slot0 + lane) * 2] : -INFINITY;
-        const float l = lane < S ? p.part_ml[(slot0 + lane) * 2 + 1] : 0.f;
-        float M = m;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        const float2* ml = (const float2*)p.part_ml + slot0;
+        float M = -INFINITY;
+        for (int sp = 0; sp < S; ++sp) M = fmaxf(M, ml[sp].x);
         const float Mu = M == -INFINITY ? 0.f : M;
-        const float w = lane < S ? fast_exp2(m - Mu) : 0.f;
-        float L = w * l;
+        float acc[DPT];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+        for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+        float L = 0.f;
+#pragma unroll 4
+        for (int sp = 0; sp < S; ++sp) {
+            const float2 v = ml[sp];
+            const float w = fast_exp2(v.x - Mu);
+            L += w * v.y;
+            const f32x4* src = (const f32x4*)(p.part_o + (slot0 + sp) * D + part * DPT);
+#pragma unroll
+            for (int k = 0; k < DPT / 4; ++k) {
+                const f32x4 x = src[k];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[k * 4 + u] += w * x[u];
+            }
+        }
         const float inv = L > 0.f ? p.v_descale / L : 0.f;
         TO* orow = (TO*)p.out + (p.q_packed ? (int64_t)q_start * p.o_sn : (int64_t)b * p.o_sb) +
-                   (int64_t)h * p.o_sh + (int64_t)i * p.o_sn;
-        for (int d = lane; d < D; d += 64) {
-            float acc = 0.f;
-            for (int sp = 0; sp < S; ++sp) {
-                const float ws = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), sp));
-                acc += ws * p.part_o[(slot0 + sp) * D + d];
-            }
-            orow[d] = (TO)(acc * inv);
-        }
+                   (int64_t)h * p.o_sh + (int64_t)i * p.o_sn + part * DPT;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) orow[e] = (TO)(acc[e] * inv);
     }
 }
 
