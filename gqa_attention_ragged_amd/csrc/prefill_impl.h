@@ -167,8 +167,16 @@ struct Prefill {
     typedef typename std::conditional<C::FP8, f16, TI>::type TO;  // output element
 
     typedef typename Vec8<T16>::type V8;
+    // fp8 kernels stage the mask tile as fp32 raw-score biases (0 / -inf for
+    // bool masks, value * log2 e / scale for additive ones) that initialize
+    // the BMM1 accumulators, so the mask costs no vector instruction per
+    // score; 16-bit kernels (whose LDS holds only 16-bit values for two
+    // workgroups per CU) stage the 16-bit values and add them per score.
+    static constexpr bool MACC = STAGED && C::FP8;
+    static constexpr int MROW = MACC ? C::BN * 4 + 16 : C::MROW;
+    static constexpr int MBYTES = 32 * MROW;
     // Bytes per pipeline stage: K tile, V tile and (mask kernels) a mask tile.
-    static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? C::MBYTES : 0);
+    static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? MBYTES : 0);
     // When a tile's copy instructions do not divide evenly over the 4 waves,
     // the waves without a last instruction still issue one (every lane out
     // of range: zeros, no memory access) into a spare 1 KiB after the stage,
@@ -239,10 +247,36 @@ struct Prefill {
         buf_load(mr, c.moff, rm);
     }
     // Staged rows hold 16-bit additive values; a bool chunk (16 keys) becomes
-    // 16 f16 values, 0 (may attend) or -inf.
-    __device__ __forceinline__ static void store_mask(char* stage, const Ctx& c, const u32x4& rm) {
+    // 16 f16 values, 0 (may attend) or -inf.  fp8 kernels (MACC) store fp32
+    // raw-score biases instead: 0 / -inf, or the additive value times kadd.
+    __device__ __forceinline__ static void store_mask(char* stage, const Ctx& c, const u32x4& rm,
+                                                      float kadd) {
         if (c.mrow_l < 0) return;
-        char* row = stage + C::STAGE + c.mrow_l * C::MROW;
+        char* row = stage + C::STAGE + c.mrow_l * MROW;
+        if constexpr (MACC) {
+            if (c.mbool) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t x = rm[w];
+                    f32x4 f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) f[u] = ((x >> (8 * u)) & 0xffu) ? 0.f : -INFINITY;
+                    *(f32x4*)(row + c.mchunk * 64 + w * 16) = f;
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < 4; w += 2) {
+                    f32x4 f;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t x = rm[w + (u >> 1)];
+                        f[u] = staged_add((x >> ((u & 1) * 16)) & 0xffffu) * kadd;
+                    }
+                    *(f32x4*)(row + c.mchunk * 32 + w * 8) = f;
+                }
+            }
+            return;
+        }
         if (c.mbool) {
             u32x4 h[2];
 #pragma unroll
@@ -272,7 +306,7 @@ struct Prefill {
     __device__ __forceinline__ static void apply_mask_raw(f32x16 (&s)[2], const char* stage,
                                                           float kadd) {
         const int lane = threadIdx.x & 63, lg = lane >> 5;
-        const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+        const char* src = stage + C::STAGE + (lane & 31) * MROW;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -333,8 +367,21 @@ struct Prefill {
     // never wait on each other's result.
     __device__ __forceinline__ static void bmm1(const char* sK, const QRegs& qreg, f32x16 (&s)[2]) {
         const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
-        s[0] = f32x16{};
-        s[1] = f32x16{};
+        if constexpr (MACC) {
+            // the staged raw-score biases of this lane's (row, keys)
+            const char* mb = sK + C::STAGE + lr * MROW;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4 v = *(const f32x4*)(mb + (kb * 32 + rq * 8 + lg * 4) * 4);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) s[kb][rq * 4 + u] = v[u];
+                }
+        } else {
+            s[0] = f32x16{};
+            s[1] = f32x16{};
+        }
         const char* row0 = sK + lr * C::KROW;
         const char* row1 = sK + (32 + lr) * C::KROW;
 #pragma unroll
@@ -417,9 +464,16 @@ struct Prefill {
             for (int rq = 0; rq < 4; ++rq) {
                 const int jg = j0 + kb * 32 + rq * 8 + lg * 4;
                 MaskGroup mg;
-                if constexpr (STAGED) {
+                if constexpr (MACC) {
+                    // the bias is in the scores already; -inf marks a removed key
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        mg.add[u] = s[kb][rq * 4 + u] == -INFINITY ? -INFINITY : 0.f;
+                        mg.ok[u] = true;
+                    }
+                } else if constexpr (STAGED) {
                     // staged tile: row = this lane's row within the 32-row tile
-                    const char* src = stage + C::STAGE + (lane & 31) * C::MROW;
+                    const char* src = stage + C::STAGE + (lane & 31) * MROW;
                     const int ko = kb * 32 + rq * 8 + lg * 4;
                     const u32x2 w = *(const u32x2*)(src + ko * 2);
 #pragma unroll
@@ -559,11 +613,11 @@ struct Prefill {
         const bool mlds = STAGED;
         if (c.t0 < c.t1) {
             if constexpr (PRIMED) {
-                if (mlds) store_mask(st0, c, rm0);
+                if (mlds) store_mask(st0, c, rm0, kadd);
             } else {
                 dma_tile(p, c, c.t0, with_v, st0, wave);
                 if (mlds) load_mask(p, c, c.t0, rm);
-                if (mlds) store_mask(st0, c, rm);
+                if (mlds) store_mask(st0, c, rm, kadd);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -610,7 +664,7 @@ struct Prefill {
                     if constexpr (STAGED) {
                         // staged mask on raw scores, lengths / causal only
                         // where the tile is not fully allowed
-                        apply_mask_raw(s, stage, kadd);
+                        if constexpr (!MACC) apply_mask_raw(s, stage, kadd);
                         if (!cl_full(p, c, it)) predicate_raw(c, it, s);
                     } else if constexpr (HAS_MASK) {
                         predicate(p, c, it, s, sc, ac, false, stage);
@@ -687,7 +741,7 @@ struct Prefill {
                     }
                 }
             }
-            if (mlds && more) store_mask(nstage, c, rm);
+            if (mlds && more) store_mask(nstage, c, rm, kadd);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's part of tile it+1 landed
             __syncthreads();
         };
