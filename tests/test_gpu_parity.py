@@ -136,6 +136,26 @@ def test_non_positive_scale(scale, kind):
     parity.compare(c, parity.run_gpu(c))
 
 
+@pytest.mark.parametrize("mask", ["bool", "f16", "bf16"])
+@pytest.mark.parametrize("norm,qdq", [("softmax", "fp8"), ("none", "fp8")])
+def test_fp8_staged_masks(mask, norm, qdq):
+    # fp8 kernels stage head-broadcast masks as fp32 raw-score biases that
+    # initialize the score accumulators: bool (0 / -inf), additive f16 / bf16
+    # values (some -inf), under each normalization.
+    seed = 280 + ["bool", "f16", "bf16"].index(mask) * 2 + ["softmax", "none"].index(norm)
+    ql = np.array([31, 1, 70, 33, 17])
+    kl = np.array([301, 40, 333, 77, 19])
+    c = synth.generate(seed=seed, q_lens=ql, kv_lens=np.maximum(kl, ql), num_heads=8,
+                       kv_num_heads=2, head_dim=128, query_form="packed_nhd",
+                       kv_form="padded_bhnd", n_kv=640, q_slack=2, kv_slack=0,
+                       dtype=torch.float8_e4m3fn, dist="round_normal", mask_kind=mask,
+                       mask_p=0.2, mask_value=-3.0 if seed % 2 else -float("inf"),
+                       mask_diag_true=True, causal_kind="lower_right", norm=norm, qdq=qdq,
+                       qscale=float(np.float32(1 / 448.0)), device=DEV,
+                       name=f"fp8-staged-{mask}-{norm}-{qdq}")
+    parity.compare(c, parity.run_gpu(c))
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", [(4, 4), (8, 4), (8, 2), (8, 1), (12, 4), (6, 2)])
 def test_head_groups_and_head_size(D, heads):
