@@ -409,6 +409,19 @@ struct Prefill {
                 s[1] = mfma32(a1, qreg[ks], s[1]);
             }
         }
+        if constexpr (!C::FP8 && C::QSTEPS == 8) {
+            // Schedule: eight K operand reads in flight ahead of the MFMAs
+            // (the default schedule waited on each pair just before its
+            // MFMAs, exposing the LDS latency): 8 reads, then 2 MFMAs and 2
+            // reads four times, then the last 8 MFMAs.
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        }
     }
 
     // Whether the tile is fully allowed by the lengths and the causal rule
