@@ -168,7 +168,15 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
 
 /* Bytes of device workspace gqa_attn_forward needs for args (0 when the
  * selected kernels need none).  Returns a gqa_status_t; *bytes is written
- * on success. */
+ * on success.
+ *
+ * The kernel plan (and with it the workspace size) is chosen per call from
+ * the shapes.  Three environment variables, read at each call, override it
+ * for measurement: GQA_ATTN_DECODE_SPLIT (keys per decode split, a power of
+ * two in 128..8192), GQA_ATTN_PREFILL_SPLITS (key slices of the prefill
+ * split-KV path, 1..32) and GQA_ATTN_XCD_REMAP=0 (no XCD-aware workgroup
+ * order).  Query the workspace size with the same environment as the
+ * forward call. */
 int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 
 /* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
