@@ -386,7 +386,9 @@ def main() -> int:
         for cfg in WORKLOADS:
             if cfg == a.workload or cfg == "1":
                 continue
-            r = measure(cfg, max(5, a.steps // 2), max(2, a.warmup // 3))
+            # the same warm-up as the headline workload: the clocks need
+            # about 150 launches to settle
+            r = measure(cfg, max(5, a.steps // 2), a.warmup)
             r.pop("_case")
             secondary[cfg] = r
             torch.cuda.empty_cache()
