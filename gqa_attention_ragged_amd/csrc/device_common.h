@@ -113,12 +113,14 @@ __device__ __forceinline__ bf16 to_t(float x, bf16*) { return (bf16)x; }
 __device__ __forceinline__ uint32_t f32_to_e4m3_pair(float a, float b) {
     a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
     b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false) &
+           0xffffu;  // the upper half (a's bits) is masked off
 }
 // The same without the clamp, for inputs known to be in [0, 464): values in
 // [448, 464) still round to 448, only larger ones would become NaN.
 __device__ __forceinline__ uint32_t f32_to_e4m3_pair_unsat(float a, float b) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false) &
+           0xffffu;  // the upper half (a's bits) is masked off
 }
 // Four fp32 values -> one dword of E4M3FN codes (a, b, c, d in bytes 0..3),
 // round to nearest even; SAT clamps to +-448 first (see above).  The second
@@ -131,7 +133,10 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
         c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
         d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
     }
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    // The first conversion keeps the upper half of its `old` operand, which
+    // the second one overwrites: passing a's own bits (dead after this) lets
+    // the result reuse a's register instead of zeroing a fresh one.
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 template <int BYTE>
