@@ -286,6 +286,24 @@ def test_workload_sampled(cfg):
 
 
 # ------------------------------------------------------------- split-KV prefill
+@pytest.mark.parametrize("heads", [(8, 4), (4, 4), (6, 2)])
+def test_split_kv_prefill_row_tiles(heads):
+    # split-KV with 64- and 128-row workgroups (group sizes 2 and 1) and a
+    # group of 3 heads: the merge walks every row of the larger row tiles
+    hq, hkv = heads
+    seed = 960 + hq * 3 + hkv
+    rng = np.random.default_rng(seed)
+    ql = np.array([130, 3, 70])
+    kl = np.maximum(np.array([3000, 900, 2100]) + rng.integers(0, 64, size=3), ql)
+    c = synth.generate(seed=seed, q_lens=ql, kv_lens=kl, num_heads=hq, kv_num_heads=hkv,
+                       head_dim=128, query_form="packed_nhd", kv_form="packed_nhd",
+                       q_slack=2, kv_slack=2, dtype=torch.float16, causal_kind="lower_right",
+                       device=DEV, name=f"splitkv-rows-{hq}/{hkv}")
+    args = capi.make_args(c.q, c.k, c.v, c.mask, c.q, **c.kwargs())
+    assert capi.gqa_attn_workspace_size(args) > 0  # the split path is taken
+    parity.compare(c, parity.run_gpu(c))
+
+
 @pytest.mark.parametrize("causal,mask", [("lower_right", None), ("lower_right", "f16"),
                                          ("none", "bool"), ("upper_left", None)])
 @pytest.mark.parametrize("dtype,D", [(torch.float16, 128), (torch.bfloat16, 64)])
