@@ -52,7 +52,7 @@ struct AttnParams {
     int32_t hq, hkv, group;           // group = hq / hkv
     int32_t heads_per_wg, rows_per_wg;
     // decode split-KV
-    float* part_o;                    // [B, Hq, S, D]
+    float* part_o;                    // [B, Hq, S, D] (prefill, f16 output: f16 O_s / l_s)
     float* part_ml;                   // [B, Hq, S, 2]
     int32_t split_keys, n_splits;
     int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs

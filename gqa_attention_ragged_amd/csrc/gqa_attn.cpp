@@ -56,6 +56,7 @@ struct Plan {
     int q_elem = 0, kv_elem = 0, head_dim = 0;
     int grid_x = 0, grid_y = 0;
     size_t workspace = 0;
+    size_t part_bytes = 4;  // prefill split-KV: bytes per partial O element
 };
 
 // Checks that a Q/K/V/Y tensor has the rank of its form and a contiguous,
@@ -383,7 +384,10 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
             const int64_t rows = qf == GQA_FORM_PACKED_NHD ? Tq : B * Nq;
             p.n_splits = (int)S;
             p.split_keys = (int)(per_tiles * 64);
-            plan->workspace = (size_t)rows * Hq * S * (D + 2) * sizeof(float) + 256;
+            // partial O: f16 (normalized per slice) when the output is f16,
+            // fp32 otherwise; (m, l) fp32
+            plan->part_bytes = qdt == GQA_DT_BF16 ? 4 : 2;
+            plan->workspace = (size_t)rows * Hq * S * (D * plan->part_bytes + 2 * sizeof(float)) + 256;
         }
     }
     // the remap linearizes the grid in 32-bit arithmetic
@@ -432,7 +436,7 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
                                                  : (int64_t)plan.p.batch * plan.p.n_q;
             const int64_t slots = rows * plan.p.hq * plan.p.n_splits;
             plan.p.part_o = (float*)w;
-            plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
+            plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * plan.part_bytes);
         }
         e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
     }

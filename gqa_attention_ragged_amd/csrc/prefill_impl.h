@@ -1046,16 +1046,33 @@ struct Prefill {
                 if (c.i < c.q_len) {
                     const int64_t row = (p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q) + c.i;
                     const int64_t slot = (row * p.hq + h) * p.n_splits + bz;
-                    float* po = p.part_o + slot * D;
+                    if constexpr (std::is_same<TO, f16>::value) {
+                        // f16 output: the slice's normalized O (a convex
+                        // combination of V rows, so within V's range) as f16
+                        const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+                        f16* po = (f16*)p.part_o + slot * D;
+                        typedef f16 h4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-                    for (int db = 0; db < D / 32; ++db)
+                        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                        for (int rq = 0; rq < 4; ++rq) {
-                            f32x4 w;
+                            for (int rq = 0; rq < 4; ++rq) {
+                                h4 w;
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
-                            *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
-                        }
+                                for (int u = 0; u < 4; ++u) w[u] = (f16)(o[db][rq * 4 + u] * inv_l);
+                                *(h4*)(po + db * 32 + rq * 8 + lg * 4) = w;
+                            }
+                    } else {
+                        float* po = p.part_o + slot * D;
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                            for (int rq = 0; rq < 4; ++rq) {
+                                f32x4 w;
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
+                                *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
+                            }
+                    }
                     if (lg == 0) {
                         p.part_ml[slot * 2] = m_run;
                         p.part_ml[slot * 2 + 1] = l_tot;
@@ -1160,12 +1177,25 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
             const float2 v = ml[sp];
             const float w = fast_exp2(v.x - Mu);
             L += w * v.y;
-            const f32x4* src = (const f32x4*)(p.part_o + (slot0 + sp) * D + part * DPT);
+            if constexpr (std::is_same<TO, f16>::value) {
+                // f16 partials hold O_s / l_s: weight w l_s
+                typedef f16 h8 __attribute__((ext_vector_type(8)));
+                const float wl = w * v.y;
+                const h8* src = (const h8*)((const f16*)p.part_o + (slot0 + sp) * D + part * DPT);
 #pragma unroll
-            for (int k = 0; k < DPT / 4; ++k) {
-                const f32x4 x = src[k];
+                for (int k = 0; k < DPT / 8; ++k) {
+                    const h8 x = src[k];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[k * 4 + u] += w * x[u];
+                    for (int u = 0; u < 8; ++u) acc[k * 8 + u] += wl * (float)x[u];
+                }
+            } else {
+                const f32x4* src = (const f32x4*)(p.part_o + (slot0 + sp) * D + part * DPT);
+#pragma unroll
+                for (int k = 0; k < DPT / 4; ++k) {
+                    const f32x4 x = src[k];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[k * 4 + u] += w * x[u];
+                }
             }
         }
         const float inv = L > 0.f ? p.v_descale / L : 0.f;
