@@ -126,18 +126,37 @@ def make_step(case):
     return step
 
 
-def time_steps(step, steps: int, warmup: int) -> float:
-    """Average ms per step over `steps` timed launches (HIP events)."""
+# The GPU raises its clocks over the first tens of milliseconds of
+# back-to-back work (measured on the prefill workload: 0.37 -> 0.28 ms per
+# step over ~100 steps); warming up for at least this long, whatever the
+# requested step count, makes the timed steps steady state.
+MIN_WARMUP_MS = 400.0
+_warmup_log: dict = {}
+
+
+def time_steps(step, steps: int, warmup: int, tag: str = "") -> float:
+    """Average ms per step over `steps` timed launches (HIP events on the
+    stream the kernels run on), after `warmup` steps and as many more as it
+    takes to reach MIN_WARMUP_MS of warm-up (recorded in _warmup_log)."""
     import torch
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    extra = 0
+    while (time.perf_counter() - t0) * 1e3 < MIN_WARMUP_MS:
+        for _ in range(10):
+            step()
+        extra += 10
+        torch.cuda.synchronize()
+    _warmup_log[tag] = {"extra_steps": extra, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
+    start.record(stream)
     for _ in range(steps):
         step()
-    end.record()
+    end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
@@ -159,7 +178,7 @@ def measure_kv_update(steps: int, warmup: int) -> dict:
         if st != 0:
             raise capi.GqaError(st, capi.last_error())
 
-    ms = time_steps(step, steps, warmup)
+    ms = time_steps(step, steps, warmup, "kvu")
     H, D = c.past_cache.shape[1], c.past_cache.shape[3]
     byts = 2 * int(np.sum(c.counts)) * H * D * c.past_cache.element_size()
     gbs = byts / (ms * 1e-3) / 1e9
@@ -177,10 +196,12 @@ def measure(cfg: str, steps: int, warmup: int) -> dict:
     case = synth.make_config(cfg, device="cuda")
     torch.cuda.synchronize()
     w = work_of(case)
-    ms = time_steps(make_step(case), steps, warmup)
+    ms = time_steps(make_step(case), steps, warmup, cfg)
     dt = dtype_name(case)
     r = {"workload": cfg, "description": synth.DESCRIPTIONS[cfg], "ms_per_step": round(ms, 4),
          "dtype": dt}
+    if cfg == "1":
+        r["latency_us"] = round(ms * 1e3, 2)  # one call, latency-bound
     if w["kind"] == "decode":
         gbs = w["bytes"] / (ms * 1e-3) / 1e9
         r.update(metric="KV GB/s", value=round(gbs, 1), unit="GB/s", bytes=w["bytes"],
@@ -204,6 +225,45 @@ def traffic_for(cfg: str, kind: str):
     if t.get("kernel_sha") != kernel_sha(kind):
         return None
     return int(t["hbm_bytes_per_launch"])
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n: int) -> None:
+    """Set the OpenMP thread count of the oracle's parallel regions."""
+    import ctypes
+    try:
+        ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+    except OSError:
+        pass
+
+
+def oracle_cfg1_ms() -> dict:
+    """The oracle on the whole tiny workload (every row), on one thread and
+    on all the process's cores: ms per call (best of 3)."""
+    import oracle
+    from gqa_attention_ragged_amd import synth
+    c = synth.make_config("1", device="cpu")
+    out = {}
+    for tag, n in (("1thread", 1), ("all_cores", int(os.environ["OMP_NUM_THREADS"]))):
+        _omp_threads(n)
+        best = 1e30
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.attention(c.q, c.k, c.v, c.mask, **c.kwargs())
+            best = min(best, time.perf_counter() - t0)
+        out[f"ms_{tag}"] = round(best * 1e3, 3)
+    _omp_threads(int(os.environ["OMP_NUM_THREADS"]))
+    return out
 
 
 def cpu_baseline(case, seconds: float) -> dict:
@@ -261,8 +321,31 @@ def cpu_baseline(case, seconds: float) -> dict:
         val = done_work / t_all / 1e9
         unit = "GB/s"
         desc = f"{len(rows)} sampled (b, head) rows, {done_work:.3e} KV bytes"
+    # the same oracle on one thread, over the first rows of the sample
+    # (about a tenth of the time budget)
+    r1 = rows[: max(1, len(rows) // (10 * max(1, int(os.environ["OMP_NUM_THREADS"]))))]
+    _omp_threads(1)
+    t1, w1 = 0.0, 0
+    for b in np.unique(r1[:, 0]):
+        sel = r1[:, 0] == b
+        sub = parity.subcase(case, [int(b)])
+        r = r1[sel].copy()
+        r[:, 0] = 0
+        t0 = time.perf_counter()
+        res = oracle.attention(sub.q, sub.k, sub.v, sub.mask, rows=r, **sub.kwargs())
+        t1 += time.perf_counter() - t0
+        if w["kind"] == "prefill":
+            w1 += int(res.nallowed.sum()) * 4 * D
+        else:
+            w1 += int(sel.sum()) * int(case.kv_lens[b]) * D * 2 * case.k.element_size()
+    _omp_threads(int(os.environ["OMP_NUM_THREADS"]))
+    v1 = w1 / t1 / (1e12 if w["kind"] == "prefill" else 1e9)
     return {"value": float(f"{val:.6g}"), "unit": unit, "cores": int(os.environ["OMP_NUM_THREADS"]),
-            "kind": "oracle", "sample": desc, "seconds": round(t_all, 2)}
+            "kind": "oracle", "sample": desc, "seconds": round(t_all, 2),
+            "host_cpu": host_cpu_model(),
+            "value_1thread": float(f"{v1:.6g}"),
+            "sample_1thread": f"{len(r1)} of those rows on one thread, {t1:.2f} s",
+            "tiny_workload_oracle": oracle_cfg1_ms()}
 
 
 def profile_pass(cfg: str) -> None:
@@ -384,7 +467,7 @@ def main() -> int:
     secondary = {}
     if not a.no_secondary:
         for cfg in WORKLOADS:
-            if cfg == a.workload or cfg == "1":
+            if cfg == a.workload:
                 continue
             # the same warm-up as the headline workload: the clocks need
             # about 150 launches to settle
@@ -402,6 +485,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
+        # warm-up steps added beyond --warmup to reach MIN_WARMUP_MS (clocks)
+        "warmup_extra": _warmup_log.get(a.workload),
         "ms_per_step": main_r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",

@@ -114,6 +114,9 @@ def load() -> ctypes.CDLL:
         lib.gqa_attn_last_hip_error.restype = ctypes.c_int
         lib.gqa_attn_abi_version.argtypes = []
         lib.gqa_attn_abi_version.restype = ctypes.c_int
+        I32 = ctypes.POINTER(ctypes.c_int32)
+        lib.gqa_attn_check_lengths.argtypes = [P, I32, I32, I32]
+        lib.gqa_attn_check_lengths.restype = ctypes.c_int
         K = ctypes.POINTER(GqaKvUpdateArgs)
         lib.gqa_kv_cache_update_validate.argtypes = [K]
         lib.gqa_kv_cache_update_validate.restype = ctypes.c_int
@@ -189,6 +192,24 @@ def make_args(q, k, v, attn_mask=None, out=None, *, query_lengths=None, kv_lengt
 
 def gqa_attn_validate(args: GqaArgs) -> int:
     return load().gqa_attn_validate(ctypes.byref(args))
+
+
+def gqa_attn_check_lengths(args: GqaArgs, query_lengths=None, kv_lengths=None,
+                           kv_page_table=None) -> int:
+    """gqa_attn_check_lengths over host copies (numpy int32 arrays or None)
+    of the call's length arrays; returns the status code."""
+    import numpy as np
+    keep = []
+
+    def ptr(x):
+        if x is None:
+            return None
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+        keep.append(a)
+        return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    return load().gqa_attn_check_lengths(ctypes.byref(args), ptr(query_lengths), ptr(kv_lengths),
+                                         ptr(kv_page_table))
 
 
 def gqa_attn_workspace_size(args: GqaArgs) -> int:

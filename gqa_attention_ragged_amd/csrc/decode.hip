@@ -172,10 +172,15 @@ struct Decode {
             u32x4 k[2][KCH];
             u32x4 v[VINS];
         };
-        // Rows [0, k1) of this sequence: keys past the split's end read as
-        // zero without touching memory (and are masked below).
-        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase, rows_bytes(k1, p.k.sn, D, KES));
-        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase, rows_bytes(k1, p.v.sn, D, KES));
+        // Rows [k0, k1) of this sequence, the split's keys: keys past the
+        // split's end read as zero without touching memory (and are masked
+        // below).  The window starts at the split (64-bit base), so a
+        // sequence's rows may span more than 4 GiB; the host bounds one
+        // split's span (plus the prefetch past its end) below 2^32 bytes.
+        const __amdgpu_buffer_rsrc_t krs =
+            make_rsrc(kbase + (int64_t)k0 * p.k.sn * KES, rows_bytes(k1 - k0, p.k.sn, D, KES));
+        const __amdgpu_buffer_rsrc_t vrs =
+            make_rsrc(vbase + (int64_t)k0 * p.v.sn * KES, rows_bytes(k1 - k0, p.v.sn, D, KES));
         auto load = [&](Tile& t, int j0) {
             if constexpr (PAGED) {
                 // a 32-key tile lies inside one page (pages hold a power of
@@ -208,7 +213,7 @@ struct Decode {
             }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int j = j0 + kb * 16 + l16;
+                const int j = j0 - k0 + kb * 16 + l16;  // key within the split
 #pragma unroll
                 for (int kc = 0; kc < KCH; ++kc)
                     buf_load(krs, (uint32_t)(((int64_t)j * p.k.sn + kchan(kc * (KV8 ? 2 : 1), g)) * KES),
@@ -216,7 +221,7 @@ struct Decode {
             }
 #pragma unroll
             for (int i = 0; i < VINS; ++i) {
-                const int j = j0 + i * VRPI + vrow;
+                const int j = j0 - k0 + i * VRPI + vrow;
                 buf_load(vrs, (uint32_t)((int64_t)j * p.v.sn * KES + vch * 16), t.v[i]);
             }
         };

@@ -52,7 +52,7 @@ struct AttnParams {
     int32_t hq, hkv, group;           // group = hq / hkv
     int32_t heads_per_wg, rows_per_wg;
     // decode split-KV
-    float* part_o;                    // [B, Hq, S, D] (prefill, f16 output: f16 O_s / l_s)
+    float* part_o;                    // [B, Hq, S, D] unnormalized O of each key slice
     float* part_ml;                   // [B, Hq, S, 2]
     int32_t split_keys, n_splits;
     int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs
@@ -215,9 +215,20 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2& v) {
     v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
-// Bytes from a sequence's first row to the end of its row n-1 (0 if n <= 0).
+// Bytes from a window's first row to the end of its row n-1 (0 if n <= 0),
+// for windows the host has bounded below 2^32 bytes (a key tile, a split, a
+// query tile).
 __device__ __forceinline__ uint32_t rows_bytes(int n, int64_t row_stride, int d, int es) {
     return n > 0 ? (uint32_t)(((int64_t)(n - 1) * row_stride + d) * es) : 0u;
+}
+// The same in 64 bits, for a whole sequence's rows (may exceed 4 GiB).
+__device__ __forceinline__ int64_t rows_bytes64(int n, int64_t row_stride, int d, int es) {
+    return n > 0 ? ((int64_t)(n - 1) * row_stride + d) * es : 0;
+}
+// A buffer range of `rem` bytes, clamped into the 32-bit range field (the
+// loads through such a window stay within its first 2^32 - 1 bytes).
+__device__ __forceinline__ uint32_t clamp_range(int64_t rem) {
+    return rem <= 0 ? 0u : rem >= 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)rem;
 }
 
 constexpr float kLog2e = 1.4426950408889634f;

@@ -16,6 +16,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "lengths.h"
 
 namespace {
 
@@ -50,6 +51,37 @@ int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
 
 enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2 };
 
+// Draft tokens per sequence the tree variants resolve.
+constexpr int kMaxTreeDrafts = 128;
+
+// Plan overrides for measurement, read from the environment once per
+// process (the first call) rather than on every call.
+struct EnvOverrides {
+    int decode_split = 0;    // GQA_ATTN_DECODE_SPLIT: keys per decode split (0 = planner's)
+    int prefill_splits = 0;  // GQA_ATTN_PREFILL_SPLITS: prefill key slices (0 = planner's)
+    bool xcd_remap = true;   // GQA_ATTN_XCD_REMAP=0 turns the XCD-aware order off
+    bool validate = false;   // GQA_ATTN_VALIDATE=1: device-side length checks before launching
+};
+
+const EnvOverrides& env_overrides() {
+    static const EnvOverrides env = [] {
+        EnvOverrides e;
+        if (const char* s = std::getenv("GQA_ATTN_DECODE_SPLIT")) {
+            const int c = std::atoi(s);
+            if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0) e.decode_split = c;
+        }
+        if (const char* s = std::getenv("GQA_ATTN_PREFILL_SPLITS")) {
+            const int v = std::atoi(s);
+            if (v >= 1 && v <= 32) e.prefill_splits = v;
+        }
+        if (const char* s = std::getenv("GQA_ATTN_XCD_REMAP"))
+            if (std::atoi(s) == 0) e.xcd_remap = false;
+        if (const char* s = std::getenv("GQA_ATTN_VALIDATE")) e.validate = std::atoi(s) != 0;
+        return e;
+    }();
+    return env;
+}
+
 struct Plan {
     Kernel kernel = K_NONE;
     gqa::AttnParams p{};
@@ -57,6 +89,7 @@ struct Plan {
     int grid_x = 0, grid_y = 0;
     size_t workspace = 0;
     size_t part_bytes = 4;  // prefill split-KV: bytes per partial O element
+    gqa::LenCheck lc{};     // the call's device-side length preconditions
 };
 
 // Checks that a Q/K/V/Y tensor has the rank of its form and a contiguous,
@@ -76,11 +109,27 @@ int check_tensor(const gqa_tensor_t& t, const char* name, int form) {
     const int64_t align_elems = 16 / es;
     if ((uintptr_t)t.data % 16)
         return fail(GQA_ERR_UNSUPPORTED, "%s: data pointer must be 16-byte aligned", name);
-    for (int d = 0; d + 1 < t.ndim; ++d)
+    for (int d = 0; d + 1 < t.ndim; ++d) {
+        if (t.stride[d] < 0)
+            return fail(GQA_ERR_UNSUPPORTED, "%s: negative stride %d", name, d);
         if (t.stride[d] % align_elems)
             return fail(GQA_ERR_UNSUPPORTED, "%s: stride %d (%lld) must be a multiple of 16 bytes",
                         name, d, (long long)t.stride[d]);
+    }
     return GQA_OK;
+}
+
+// The kernels address one window of rows of a (sequence, head) through a
+// buffer descriptor with a 32-bit range and 32-bit offsets: a query tile
+// (32 rows), a key tile (64 rows) or a decode split.  The window's base is
+// 64-bit, so a sequence may span any number of bytes, but `rows` consecutive
+// rows of t (form's row stride) must lie within 2^32 bytes.
+bool window_fits(const gqa_tensor_t& t, int form, int64_t rows) {
+    const int64_t sn = form == GQA_FORM_PACKED_NHD ? t.stride[0] : t.stride[2];
+    const int64_t es = elem_bytes(t.dtype), D = t.shape[t.ndim - 1];
+    // (rows - 1) * sn * es + D * es < 2^32, without overflowing int64
+    const double bytes = ((double)(rows - 1) * (double)sn + (double)D) * (double)es;
+    return bytes < 4294967296.0 - 4096.0;
 }
 
 int plan_call(const gqa_attn_args_t* a, Plan* plan) {
@@ -166,6 +215,14 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     const int64_t kv_max = kf == GQA_FORM_PADDED_BHND ? Nkv : Tkv;
     if (Nq > INT32_MAX || Nkv > INT32_MAX || Tq > INT32_MAX || Tkv > INT32_MAX || B > 65535)
         return fail(GQA_ERR_UNSUPPORTED, "extents beyond the int32 / grid limits of this build");
+    if (!window_fits(a->q, qf, 32))
+        return fail(GQA_ERR_UNSUPPORTED, "q: 32 rows span 4 GiB or more (row stride too large)");
+    // key windows: a 64-key tile (prefill), a split of up to 8192 keys plus
+    // the next tile's prefetch (decode)
+    const int64_t kv_window = 8192 + 256;
+    if (!window_fits(a->k, kf, kv_window) || !window_fits(a->v, kf, kv_window))
+        return fail(GQA_ERR_UNSUPPORTED, "k/v: %lld rows span 4 GiB or more (row stride too large)",
+                    (long long)kv_window);
 
     if (a->qdq != GQA_QDQ_OFF && !(a->qscale > 0.f && std::isfinite(a->qscale)))
         return fail(GQA_ERR_INVALID_ARG, "qscale must be finite and > 0 when qdq is on");
@@ -177,6 +234,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     p = gqa::AttnParams{};
     p.mask_kind = gqa::MASK_NONE;
     const gqa_tensor_t& m = a->attn_mask;
+    int64_t mask_q = 0, mask_kv = 0;  // mask extents that must cover the lengths
     if (m.data) {
         if (m.ndim < 1 || m.ndim > 4) return fail(GQA_ERR_INVALID_ARG, "attn_mask rank must be 1..4");
         switch (m.dtype) {
@@ -191,6 +249,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
             ext[4 - m.ndim + d] = m.shape[d];
             str[4 - m.ndim + d] = m.shape[d] == 1 ? 0 : m.stride[d];
             if (m.shape[d] < 1) return fail(GQA_ERR_INVALID_ARG, "attn_mask has an empty dimension");
+            if (m.stride[d] < 0 && m.shape[d] != 1)
+                return fail(GQA_ERR_UNSUPPORTED, "attn_mask: negative stride %d", d);
         }
         if (ext[0] != 1 && ext[0] != B) return fail(GQA_ERR_INVALID_ARG, "attn_mask batch extent");
         if (ext[1] != 1 && ext[1] != Hq) return fail(GQA_ERR_INVALID_ARG, "attn_mask head extent");
@@ -198,6 +258,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
             return fail(GQA_ERR_INVALID_ARG, "attn_mask query extent < N_q");
         if (kf == GQA_FORM_PADDED_BHND && !a->kv_lengths && ext[3] != 1 && ext[3] < Nkv)
             return fail(GQA_ERR_INVALID_ARG, "attn_mask key extent < N_kv");
+        mask_q = ext[2] != 1 ? ext[2] : 0;
+        mask_kv = ext[3] != 1 ? ext[3] : 0;
         p.mask = m.data;
         p.m_sb = str[0];
         p.m_sh = str[1];
@@ -208,12 +270,38 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
                      str[1] % 4 == 0 && str[2] % 4 == 0;
     }
 
+    // the device-side preconditions on the lengths (checked on the GPU when
+    // GQA_ATTN_VALIDATE=1, or on host copies by gqa_attn_check_lengths)
+    {
+        gqa::LenCheck& lc = plan->lc;
+        lc = gqa::LenCheck{};
+        lc.batch = (int32_t)B;
+        lc.ql = a->query_lengths;
+        lc.kl = a->kv_lengths;
+        lc.ptab = paged ? a->kv_page_table : nullptr;
+        lc.q_packed = qf == GQA_FORM_PACKED_NHD;
+        lc.kv_packed = kf == GQA_FORM_PACKED_NHD;
+        lc.kv_paged = paged;
+        lc.ptab_pages = paged ? a->kv_max_pages : 0;
+        lc.page_size = paged ? (int32_t)a->k.shape[2] : 0;
+        lc.t_q = Tq;
+        lc.t_kv = Tkv;
+        lc.n_q = Nq;
+        lc.n_kv = Nkv;
+        lc.k_pages = paged ? a->k.shape[0] : 0;
+        lc.v_pages = paged ? a->v.shape[0] : 0;
+        lc.mask_q = mask_q;
+        lc.mask_kv = mask_kv;
+        lc.max_drafts = a->tree_parents ? kMaxTreeDrafts : 0;
+    }
+
     // supported combinations
     if (D != 64 && D != 128) return fail(GQA_ERR_UNSUPPORTED, "head_size must be 64 or 128");
-    // tree decoding: each wave resolves the ancestor chains of up to 64
-    // drafts per sequence (one lane per draft)
-    if (a->tree_parents && qf == GQA_FORM_PADDED_BHND && Nq > 64)
-        return fail(GQA_ERR_UNSUPPORTED, "tree_parents with padded Q needs N_q <= 64");
+    // tree decoding: each wave resolves the ancestor chains of up to 128
+    // drafts per sequence (two per lane)
+    if (a->tree_parents && qf == GQA_FORM_PADDED_BHND && Nq > kMaxTreeDrafts)
+        return fail(GQA_ERR_UNSUPPORTED, "tree_parents with padded Q needs N_q <= %d",
+                    kMaxTreeDrafts);
     if (qdt == GQA_DT_FP8_E4M3 && a->qdq != GQA_QDQ_FP8_E4M3)
         return fail(GQA_ERR_UNSUPPORTED, "fp8 Q/K/V needs fp8 Q/DQ of the scores");
     const int64_t G = Hq / Hkv;
@@ -300,11 +388,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         // fp16 and fp8 KV, against 512 .. 8192), halved while the grid has
         // fewer than 4096 workgroups; GQA_ATTN_DECODE_SPLIT (a power of two,
         // 128..8192) overrides the start value for tuning.
-        int C = 4096;
-        if (const char* e = std::getenv("GQA_ATTN_DECODE_SPLIT")) {
-            const int c = std::atoi(e);
-            if (c >= 128 && c <= 8192 && (c & (c - 1)) == 0) C = c;
-        }
+        int C = env_overrides().decode_split ? env_overrides().decode_split : 4096;
         auto nsplit = [&](int c) { return (kv_max + c - 1) / c; };
         while (C > 128 && B * Hkv * nsplit(C) < 4096) C /= 2;
         const int64_t S = kv_max > 0 ? nsplit(C) : 1;
@@ -332,8 +416,11 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         (p.mask_kind == gqa::MASK_BOOL || p.mask_kind == gqa::MASK_F16 ||
          p.mask_kind == gqa::MASK_BF16)) {
         const int64_t es = p.mask_kind == gqa::MASK_BOOL ? 1 : 2;
+        // a staged tile's 32 rows are read through one 32-bit window
+        const double span = (31.0 * (double)p.m_si + (double)m.shape[m.ndim - 1]) * (double)es;
         p.mask_lds = (uintptr_t)m.data % 16 == 0 && (p.m_si * es) % 16 == 0 &&
-                     (p.m_sb * es) % 16 == 0 && (m.shape[m.ndim - 1] * es) % 16 == 0;
+                     (p.m_sb * es) % 16 == 0 && (m.shape[m.ndim - 1] * es) % 16 == 0 &&
+                     span < 4294967296.0 - 4096.0;
     }
     int64_t gx = qf == GQA_FORM_PADDED_BHND ? B * ((Nq + R - 1) / R) : (Tq + R - 1) / R + B;
     if (gx > INT32_MAX) return fail(GQA_ERR_UNSUPPORTED, "too many query tiles");
@@ -343,9 +430,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // MI355X has 8 XCDs (each with its own L2) that receive workgroup ids in
     // turn; the prefill kernel remaps ids so that an XCD works through whole
     // head groups when they divide evenly (GQA_ATTN_XCD_REMAP=0 turns it off).
-    p.xcds = plan->grid_y % 8 == 0 ? 8 : 0;
-    if (const char* e = std::getenv("GQA_ATTN_XCD_REMAP"))
-        if (std::atoi(e) == 0) p.xcds = 0;
+    p.xcds = plan->grid_y % 8 == 0 && env_overrides().xcd_remap ? 8 : 0;
     plan->kernel = K_PREFILL;
     plan->workspace = 0;
     p.n_splits = 1;
@@ -374,19 +459,17 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
             S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
         }
         // GQA_ATTN_PREFILL_SPLITS (1..32) overrides the slice count for tuning
-        if (const char* e = std::getenv("GQA_ATTN_PREFILL_SPLITS")) {
-            const int v = std::atoi(e);
-            if (v >= 1 && v <= 32) S = std::min<int64_t>(v, std::max<int64_t>(kv_tiles, 1));
-        }
+        if (const int v = env_overrides().prefill_splits)
+            S = std::min<int64_t>(v, std::max<int64_t>(kv_tiles, 1));
         if (S > 1) {
             const int64_t per_tiles = (kv_tiles + S - 1) / S;
             S = (kv_tiles + per_tiles - 1) / per_tiles;
             const int64_t rows = qf == GQA_FORM_PACKED_NHD ? Tq : B * Nq;
             p.n_splits = (int)S;
             p.split_keys = (int)(per_tiles * 64);
-            // partial O: f16 (normalized per slice) when the output is f16,
-            // fp32 otherwise; (m, l) fp32
-            plan->part_bytes = qdt == GQA_DT_BF16 ? 4 : 2;
+            // partial O and (m, l) in fp32: the output is rounded once, in
+            // the merge
+            plan->part_bytes = 4;
             plan->workspace = (size_t)rows * Hq * S * (D * plan->part_bytes + 2 * sizeof(float)) + 256;
         }
     }
@@ -411,6 +494,24 @@ int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes) {
     return st;
 }
 
+int gqa_attn_check_lengths(const gqa_attn_args_t* args, const int32_t* query_lengths_host,
+                           const int32_t* kv_lengths_host, const int32_t* kv_page_table_host) {
+    Plan plan;
+    const int st = plan_call(args, &plan);
+    if (st != GQA_OK) return st;
+    gqa::LenCheck lc = plan.lc;
+    if ((lc.ql && !query_lengths_host) || (lc.kl && !kv_lengths_host) ||
+        (lc.ptab && !kv_page_table_host))
+        return fail(GQA_ERR_INVALID_ARG, "a host copy of every length array the call uses is needed");
+    lc.ql = lc.ql ? query_lengths_host : nullptr;
+    lc.kl = lc.kl ? kv_lengths_host : nullptr;
+    lc.ptab = lc.ptab ? kv_page_table_host : nullptr;
+    uint32_t e = 0;
+    for (int b = 0; b < lc.batch; ++b) e |= gqa::check_sequence(lc, b);
+    if (e) return fail(GQA_ERR_INVALID_ARG, "lengths: %s", gqa::len_error_text(e));
+    return GQA_OK;
+}
+
 int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
                      void* stream) {
     Plan plan;
@@ -419,6 +520,22 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
     if (plan.kernel == K_NONE) return GQA_OK;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
+    if (env_overrides().validate && plan.lc.batch > 0) {
+        // debug mode: check the lengths on the device, wait for the verdict,
+        // and launch nothing if they break a precondition
+        uint32_t* status = nullptr;
+        uint32_t bits = 0;
+        e = gqa::length_status_ptr(&status);
+        if (e == hipSuccess) e = gqa::launch_length_check(plan.lc, status, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(&bits, status, sizeof bits, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) {
+            g_hip_err = (int)e;
+            return fail(GQA_ERR_HIP, "length check failed: %s", hipGetErrorString(e));
+        }
+        if (bits) return fail(GQA_ERR_INVALID_ARG, "lengths (device check): %s",
+                              gqa::len_error_text(bits));
+    }
     if (plan.kernel == K_DECODE) {
         if (!workspace || workspace_bytes < plan.workspace)
             return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed", plan.workspace);
@@ -553,6 +670,6 @@ const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_last_hip_error(void) { return g_hip_err; }
 
-int gqa_attn_abi_version(void) { return 4; }
+int gqa_attn_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -13,10 +13,6 @@ enum Elem { ELEM_F16 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2 };
 hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
                           hipStream_t stream);
 
-// Split-KV combine of the prefill kernel (when n_splits > 1).
-hipError_t launch_prefill_combine(const AttnParams& p, int elem, int head_dim, int grid_x,
-                                  hipStream_t stream);
-
 // The general prefill kernels of one element type (launch_prefill's parts).
 hipError_t launch_prefill_f16(const AttnParams& p, int head_dim, int grid_x, int grid_y,
                               hipStream_t stream);
@@ -29,6 +25,13 @@ hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, int grid_x, int
 // q_elem: Q type (f16/bf16); kv_elem: K/V type (same as q, or fp8).
 hipError_t launch_decode(const AttnParams& p, int q_elem, int kv_elem, int head_dim,
                          hipStream_t stream);
+
+// Length-check kernel (GQA_ATTN_VALIDATE=1): writes the OR of the
+// violation bits of every sequence (lengths.h) to *status.
+struct LenCheck;
+hipError_t launch_length_check(const LenCheck& c, uint32_t* status, hipStream_t stream);
+// Device address of this device's status word for the length check.
+hipError_t length_status_ptr(uint32_t** out);
 
 // KV-cache update (TRT_KVCacheUpdate, linear mode).  Element strides; the
 // row of (b, h, n) of the cache / output starts at base + b*sb + h*sh + n*sn

@@ -1,23 +1,10 @@
-// prefill.hip -- launchers of the general prefill kernel (the kernels are
+// prefill.hip -- launcher of the general prefill kernel (the kernels are
 // templates in prefill_impl.h, instantiated per element type in
 // prefill_f16.hip, prefill_bf16.hip and prefill_fp8.hip so that the three
-// compile in parallel) and of the split-KV combine kernel.
-#include "prefill_impl.h"
+// compile in parallel; each launches its split-KV combine itself).
+#include "launch.h"
 
 namespace gqa {
-
-hipError_t launch_prefill_combine(const AttnParams& p, int elem, int head_dim, int grid_x,
-                                  hipStream_t stream) {
-    const dim3 grid(grid_x, p.hq);
-    if (elem == ELEM_BF16) {
-        if (head_dim == 64) hipLaunchKernelGGL((prefill_combine_kernel<bf16, 64>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((prefill_combine_kernel<bf16, 128>), grid, dim3(256), 0, stream, p);
-    } else {
-        if (head_dim == 64) hipLaunchKernelGGL((prefill_combine_kernel<f16, 64>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((prefill_combine_kernel<f16, 128>), grid, dim3(256), 0, stream, p);
-    }
-    return hipGetLastError();
-}
 
 hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
                           hipStream_t stream) {

@@ -206,44 +206,73 @@ struct Prefill {
         int wave_kv_end;      // keys this wave can see (causal)
         const char* kbase;    // K rows of (b, kv head)
         const char* vbase;
-        uint32_t kbytes, vbytes;        // bytes from row 0 to the end of the last valid key
-        uint32_t ktile, vtile;          // bytes per tile of BN keys
+        int64_t kbytes, vbytes;         // bytes from row 0 to the end of the last valid key
+        int64_t ktile, vtile;           // bytes per tile of BN keys
         uint32_t koff[C::KMAX], voff[C::VMAX];  // this lane's source offsets inside a tile
         const char* mrow;     // mask row of this lane's query row (or null)
         const char* mtile;    // staged mask: the workgroup's first mask row
-        uint32_t mvalid;      // staged mask: bytes up to the last valid (row, key)
+        int64_t mvalid;       // staged mask: bytes up to the last valid (row, key)
         uint32_t moff;        // staged mask: this thread's load offset in a tile
         int mrow_l, mchunk;   // staged mask: this thread's (row, 16-byte chunk); row < 0: idle
         bool mbool;           // staged mask: bool source (converted to f16 0 / -inf)
         int i;                // this lane's query row
         bool tree;            // tree decoding: the last q_len keys are draft tokens
         int tbase;            // key of draft 0 (kv_len - q_len)
-        uint32_t anc_lo, anc_hi;  // drafts on this row's ancestor chain (bit t = draft t)
+        // drafts on this row's ancestor chain, itself included: bit t % 32 of
+        // word t / 32 is draft t (four words, no arrays: a lane-dependent
+        // array index would put the context in scratch memory)
+        uint32_t anc0, anc1, anc2, anc3;
+        bool tree_over;       // row beyond the drafts this build resolves: its output is NaN
     };
 
+    // Drafts per sequence whose ancestor chains the tree variants resolve
+    // (two per lane).
+    static constexpr int kMaxDrafts = 128;
+
     // Tree rule for draft t (key tbase + t) of this lane's row: the row's own
-    // draft and its ancestors (rows beyond the first 64 drafts: itself only).
+    // draft and its ancestors.
+    // Both halves are read and the bit is picked arithmetically: a select
+    // between two fields of the context would become a load through a
+    // selected pointer, which keeps the whole context in scratch memory.
     __device__ __forceinline__ static bool tree_ok(const Ctx& c, int t) {
-        const uint32_t w = t < 32 ? c.anc_lo : c.anc_hi;
-        return t == c.i || (t < 64 && ((w >> (t & 31)) & 1u));
+        const uint64_t lo = ((uint64_t)c.anc1 << 32) | c.anc0;
+        const uint64_t hi = ((uint64_t)c.anc3 << 32) | c.anc2;
+        const uint32_t sh = (uint32_t)t & 63u;
+        const uint64_t b = ((lo >> sh) & (uint64_t)(t < 64)) |
+                           ((hi >> sh) & (uint64_t)(t >= 64 && t < kMaxDrafts));
+        return (b & 1u) != 0;
+    }
+
+    // Rows past the drafts the tree variants resolve output NaN: the result
+    // is visibly undefined rather than computed by another rule.
+    __device__ __forceinline__ static void poison_over(const Ctx& c, ORegs& o) {
+        if constexpr (TREE) {
+            if (c.tree_over) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[db][r] = __builtin_nanf("");
+            }
+        }
     }
 
     // A buffer window starting at tile `tile`: the wave-uniform base moves
-    // with the tile (scalar arithmetic only) and the range ends with the last
-    // valid key, so keys >= kv_len read as zero and touch no memory.
+    // with the tile (64-bit scalar arithmetic, so a sequence's rows may span
+    // more than 4 GiB) and the range ends with the last valid key, so keys
+    // >= kv_len read as zero and touch no memory.  One tile's loads reach at
+    // most BN rows past the base (the host bounds that below 2^32 bytes).
     __device__ __forceinline__ static __amdgpu_buffer_rsrc_t window(const char* base,
-                                                                    uint32_t valid,
-                                                                    uint32_t stride, int tile) {
-        const uint32_t off = (uint32_t)tile * stride;
-        return make_rsrc(base + off, valid > off ? valid - off : 0u);
+                                                                    int64_t valid,
+                                                                    int64_t stride, int tile) {
+        const int64_t off = (int64_t)tile * stride;
+        return make_rsrc(base + off, clamp_range(valid - off));
     }
 
     __device__ __forceinline__ static void load_mask(const AttnParams& p, const Ctx& c, int tile,
                                                      u32x4& rm) {
         const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
-        const uint32_t off = (uint32_t)tile * (uint32_t)(C::BN * es);
-        const __amdgpu_buffer_rsrc_t mr =
-            make_rsrc(c.mtile + off, c.mvalid > off ? c.mvalid - off : 0u);
+        const int64_t off = (int64_t)tile * (C::BN * es);
+        const __amdgpu_buffer_rsrc_t mr = make_rsrc(c.mtile + off, clamp_range(c.mvalid - off));
         buf_load(mr, c.moff, rm);
     }
     // Staged rows hold 16-bit additive values; a bool chunk (16 keys) becomes
@@ -810,7 +839,8 @@ struct Prefill {
         c.causal = p.causal != 0;
         c.tree = TREE && p.tree != nullptr;
         c.tbase = c.kv_len - c.q_len;
-        c.anc_lo = c.anc_hi = 0u;
+        c.anc0 = c.anc1 = c.anc2 = c.anc3 = 0u;
+        c.tree_over = false;
         const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
         const int hw = p.heads_per_wg;
         const int h = by * hw + (wave % hw);
@@ -819,31 +849,70 @@ struct Prefill {
         c.i = c.wr0 + lr;
         c.wave_rows = c.wr0 < c.q_len;
         if (TREE && c.tree) {
-            // Ancestor sets of the sequence's first 64 drafts by pointer
-            // jumping, lane l = draft l: A_l starts as {l} and J_l as its
-            // parent; each round A_l |= A_{J_l}, J_l = J_{J_l} doubles the
-            // chain length covered, so 6 rounds cover any chain of 64.
+            // Ancestor sets of the sequence's first 128 drafts by pointer
+            // jumping, lane l holding drafts l and l + 64: a draft's set A
+            // starts as itself and its jump J as its parent; each round
+            // A |= A of J, J = J of J doubles the chain length covered, so 7
+            // rounds cover any chain of 128.  Parents precede their children,
+            // so every jump of draft l (< 64) stays below 64: its set lives
+            // in the low 64 bits and needs its own half only.
             const int64_t prow = p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q;
-            int par = lane < c.q_len ? p.tree[prow + lane] : -1;
-            int jmp = (par >= 0 && par < lane) ? par : -1;
-            uint32_t a_lo = lane < c.q_len && lane < 32 ? 1u << lane : 0u;
-            uint32_t a_hi = lane < c.q_len && lane >= 32 ? 1u << (lane - 32) : 0u;
+            const int d1 = lane + 64;
+            const int par0 = lane < c.q_len ? p.tree[prow + lane] : -1;
+            const int par1 = d1 < c.q_len ? p.tree[prow + d1] : -1;
+            int j0 = (par0 >= 0 && par0 < lane) ? par0 : -1;
+            int j1 = (par1 >= 0 && par1 < d1) ? par1 : -1;
+            // draft l: words 0, 1 of its set; draft l + 64: words 0..3
+            const uint32_t self = 1u << (lane & 31);
+            uint32_t a0w0 = lane < c.q_len && lane < 32 ? self : 0u;
+            uint32_t a0w1 = lane < c.q_len && lane >= 32 ? self : 0u;
+            uint32_t a1w0 = 0u, a1w1 = 0u;
+            uint32_t a1w2 = d1 < c.q_len && lane < 32 ? self : 0u;
+            uint32_t a1w3 = d1 < c.q_len && lane >= 32 ? self : 0u;
 #pragma unroll
-            for (int round = 0; round < 6; ++round) {
-                const int src = jmp >= 0 ? jmp : lane;
-                const uint32_t o_lo = __shfl(a_lo, src), o_hi = __shfl(a_hi, src);
-                const int o_j = __shfl(jmp, src);
-                if (jmp >= 0) {
-                    a_lo |= o_lo;
-                    a_hi |= o_hi;
-                    jmp = o_j;
+            for (int round = 0; round < 7; ++round) {
+                // every lane reads its sources' values of this round first
+                const int s0 = j0 >= 0 ? j0 : lane;
+                const uint32_t f0 = __shfl(a0w0, s0), f1 = __shfl(a0w1, s0);
+                const int fj = __shfl(j0, s0);
+                const int s1 = j1 >= 0 ? (j1 & 63) : lane;
+                const uint32_t g0 = __shfl(a0w0, s1), g1 = __shfl(a0w1, s1);
+                const int gj = __shfl(j0, s1);
+                const uint32_t h0 = __shfl(a1w0, s1), h1 = __shfl(a1w1, s1);
+                const uint32_t h2 = __shfl(a1w2, s1), h3 = __shfl(a1w3, s1);
+                const int hj = __shfl(j1, s1);
+                if (j0 >= 0) {
+                    a0w0 |= f0;
+                    a0w1 |= f1;
+                    j0 = fj;
+                }
+                if (j1 >= 64) {  // the jump lands on a draft of the upper half
+                    a1w0 |= h0;
+                    a1w1 |= h1;
+                    a1w2 |= h2;
+                    a1w3 |= h3;
+                    j1 = hj;
+                } else if (j1 >= 0) {
+                    a1w0 |= g0;
+                    a1w1 |= g1;
+                    j1 = gj;
                 }
             }
+            // this lane's row: draft i's set from lane i % 64
             const int mine = c.i & 63;
-            const uint32_t m_lo = __shfl(a_lo, mine), m_hi = __shfl(a_hi, mine);
+            const uint32_t m0 = __shfl(a0w0, mine), m1 = __shfl(a0w1, mine);
+            const uint32_t u0 = __shfl(a1w0, mine), u1 = __shfl(a1w1, mine);
+            const uint32_t u2 = __shfl(a1w2, mine), u3 = __shfl(a1w3, mine);
             if (c.i < 64) {
-                c.anc_lo = m_lo;
-                c.anc_hi = m_hi;
+                c.anc0 = m0;
+                c.anc1 = m1;
+            } else if (c.i < kMaxDrafts) {
+                c.anc0 = u0;
+                c.anc1 = u1;
+                c.anc2 = u2;
+                c.anc3 = u3;
+            } else {
+                c.tree_over = c.i < c.q_len;
             }
         }
         const int wg_last = min(row0 + R, c.q_len) - 1;
@@ -875,10 +944,10 @@ struct Prefill {
                             : p.kv_packed ? (int64_t)kv_start * p.v.sn : (int64_t)b * p.v.sb;
         c.kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * C::ES;
         c.vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * C::ES;
-        c.kbytes = rows_bytes(c.kv_len, p.k.sn, D, C::ES);
-        c.vbytes = rows_bytes(c.kv_len, p.v.sn, D, C::ES);
-        c.ktile = (uint32_t)((int64_t)C::BN * p.k.sn * C::ES);
-        c.vtile = (uint32_t)((int64_t)C::BN * p.v.sn * C::ES);
+        c.kbytes = rows_bytes64(c.kv_len, p.k.sn, D, C::ES);
+        c.vbytes = rows_bytes64(c.kv_len, p.v.sn, D, C::ES);
+        c.ktile = (int64_t)C::BN * p.k.sn * C::ES;
+        c.vtile = (int64_t)C::BN * p.v.sn * C::ES;
         {
             // source of the 16 LDS bytes this lane writes in each copy
             // instruction: K rows are padded (positions in the pad read as
@@ -923,9 +992,7 @@ struct Prefill {
             // bytes, so the rounded end stays inside that row): a partially
             // valid chunk would otherwise be range-checked out as zeros.
             const int64_t kend = ((int64_t)c.kv_len * es + 15) & ~(int64_t)15;
-            c.mvalid = rows > 0 && c.kv_len > 0
-                           ? (uint32_t)((int64_t)(rows - 1) * p.m_si * es + kend)
-                           : 0u;
+            c.mvalid = rows > 0 && c.kv_len > 0 ? (int64_t)(rows - 1) * p.m_si * es + kend : 0;
             c.moff = c.mrow_l >= 0 ? (uint32_t)((int64_t)c.mrow_l * p.m_si * es + c.mchunk * 16)
                                    : 0xFFFFFFF0u;  // idle threads: out of range, no access
         }
@@ -1030,15 +1097,18 @@ struct Prefill {
         if constexpr (MODE == MODE_NONE) {
             const float inv = p.qdq ? 1.f / p.qscale : 1.f;
             sweep<PASS_NONE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o, rm0);
+            poison_over(c, o);
             if (p.qdq) factor *= p.qscale;
         } else if constexpr (MODE == MODE_SOFTMAX_QDQ || MODE == MODE_SOFTMAX_QDQ_NS) {
             sweep<PASS_STATS, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
             const float l_tot = halves_sum(l_run);
             const float inv = l_tot > 0.f ? 1.f / (l_tot * p.qscale) : 0.f;
             sweep<PASS_FIXED, MODE == MODE_SOFTMAX_QDQ>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, inv, o);
+            poison_over(c, o);
             factor *= p.qscale;
         } else {
             sweep<PASS_ONLINE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
+            poison_over(c, o);
             const float l_tot = halves_sum(l_run);
             if (nsl > 1) {
                 // split-KV: unnormalized O with its reference max and sum
@@ -1046,33 +1116,16 @@ struct Prefill {
                 if (c.i < c.q_len) {
                     const int64_t row = (p.q_packed ? (int64_t)q_start : (int64_t)b * p.n_q) + c.i;
                     const int64_t slot = (row * p.hq + h) * p.n_splits + bz;
-                    if constexpr (std::is_same<TO, f16>::value) {
-                        // f16 output: the slice's normalized O (a convex
-                        // combination of V rows, so within V's range) as f16
-                        const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-                        f16* po = (f16*)p.part_o + slot * D;
-                        typedef f16 h4 __attribute__((ext_vector_type(4)));
+                    float* po = p.part_o + slot * D;
 #pragma unroll
-                        for (int db = 0; db < D / 32; ++db)
+                    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                            for (int rq = 0; rq < 4; ++rq) {
-                                h4 w;
+                        for (int rq = 0; rq < 4; ++rq) {
+                            f32x4 w;
 #pragma unroll
-                                for (int u = 0; u < 4; ++u) w[u] = (f16)(o[db][rq * 4 + u] * inv_l);
-                                *(h4*)(po + db * 32 + rq * 8 + lg * 4) = w;
-                            }
-                    } else {
-                        float* po = p.part_o + slot * D;
-#pragma unroll
-                        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                            for (int rq = 0; rq < 4; ++rq) {
-                                f32x4 w;
-#pragma unroll
-                                for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
-                                *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
-                            }
-                    }
+                            for (int u = 0; u < 4; ++u) w[u] = o[db][rq * 4 + u];
+                            *(f32x4*)(po + db * 32 + rq * 8 + lg * 4) = w;
+                        }
                     if (lg == 0) {
                         p.part_ml[slot * 2] = m_run;
                         p.part_ml[slot * 2 + 1] = l_tot;
@@ -1115,8 +1168,17 @@ struct Prefill {
     }
 };
 
+// Two workgroups per CU (<= 256 VGPRs per wave), except the 16-bit "none"
+// normalization kernels at D = 128, whose split BMM2 needs more registers:
+// one workgroup per CU, so that no kernel uses scratch memory (scratch loads
+// would share vmcnt with the direct-to-LDS tile copies that the key loop
+// waits on by hand).
+template <typename TI, int D, int MODE>
+constexpr int kPrefillWgsPerCu =
+    MODE == MODE_NONE && D == 128 && !std::is_same<TI, fp8>::value ? 1 : 2;
+
 template <typename TI, int D, int MODE, int MK, bool PAGED = false>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, (kPrefillWgsPerCu<TI, D, MODE>)) void prefill_kernel(AttnParams p) {
     // two separate stage arrays: the compiler then knows that the copy into
     // one stage never aliases the reads of the other, and does not wait for
     // the copy before computing on the current stage
@@ -1177,25 +1239,12 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
             const float2 v = ml[sp];
             const float w = fast_exp2(v.x - Mu);
             L += w * v.y;
-            if constexpr (std::is_same<TO, f16>::value) {
-                // f16 partials hold O_s / l_s: weight w l_s
-                typedef f16 h8 __attribute__((ext_vector_type(8)));
-                const float wl = w * v.y;
-                const h8* src = (const h8*)((const f16*)p.part_o + (slot0 + sp) * D + part * DPT);
+            const f32x4* src = (const f32x4*)(p.part_o + (slot0 + sp) * D + part * DPT);
 #pragma unroll
-                for (int k = 0; k < DPT / 8; ++k) {
-                    const h8 x = src[k];
+            for (int k = 0; k < DPT / 4; ++k) {
+                const f32x4 x = src[k];
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) acc[k * 8 + u] += wl * (float)x[u];
-                }
-            } else {
-                const f32x4* src = (const f32x4*)(p.part_o + (slot0 + sp) * D + part * DPT);
-#pragma unroll
-                for (int k = 0; k < DPT / 4; ++k) {
-                    const f32x4 x = src[k];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[k * 4 + u] += w * x[u];
-                }
+                for (int u = 0; u < 4; ++u) acc[k * 4 + u] += w * x[u];
             }
         }
         const float inv = L > 0.f ? p.v_descale / L : 0.f;

@@ -56,8 +56,9 @@
  * kv_page_table[b][1][j / page_size] of v.  kv_lengths [B] is required.
  *
  * Ownership: the caller owns every buffer (all device pointers unless noted);
- * the library never allocates, frees or synchronizes on the forward path
- * and launches asynchronously on the caller's stream.
+ * the library never allocates or frees device memory on the forward path and
+ * launches asynchronously on the caller's stream (it synchronizes only in the
+ * GQA_ATTN_VALIDATE=1 debug mode described at gqa_attn_forward).
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -130,15 +131,25 @@ typedef struct {
  *      page_size and every page index a sequence uses lies in [0, P).
  * tree_parents: optional device int32, token-aligned with q's rows ([T_q]
  *      packed, [B, N_q] contiguous padded); see "Tree decoding" above.
- *      Padded q needs N_q <= 64.  Packed q: a sequence's drafts beyond the
- *      first 64 attend the context and themselves only (device-side limit
- *      of this build).
+ *      The kernels resolve the ancestor chains of up to 128 drafts per
+ *      sequence: padded q needs N_q <= 128 (GQA_ERR_UNSUPPORTED otherwise);
+ *      with packed q, the rows of a sequence past its 128th draft come out
+ *      as NaN (a device-side precondition: see below).
  *
- * Device-side length preconditions (not checked on the host, which never
- * reads device memory): lengths non-negative and monotone, query_lengths[0]
- * = kv_lengths[0] = 0 when cumulative, query_lengths[B] <= T_q,
- * kv_lengths[B] <= T_kv, q_len_b <= N_q and kv_len_b <= N_kv for padded
- * forms, and the mask's query / key extents cover q_len_b / kv_len_b. */
+ * Strides: non-negative element strides.  The kernels read a query tile
+ * (32 rows) and a key tile or decode split (up to 8448 rows) through 32-bit
+ * buffer windows whose bases are 64-bit: a sequence may span any number of
+ * bytes, but that many consecutive rows (row stride x element size) must
+ * span less than 4 GiB (GQA_ERR_UNSUPPORTED otherwise).
+ *
+ * Device-side length preconditions (the host never reads device memory, so
+ * gqa_attn_forward does not check them unless GQA_ATTN_VALIDATE=1 is set,
+ * see below): lengths non-negative and monotone, query_lengths[0] =
+ * kv_lengths[0] = 0 when cumulative, query_lengths[B] <= T_q, kv_lengths[B]
+ * <= T_kv, q_len_b <= N_q and kv_len_b <= N_kv for padded forms (paged:
+ * kv_max_pages * page_size), every page-table entry a sequence uses inside
+ * its pool, the mask's query / key extents covering q_len_b / kv_len_b, and
+ * with tree_parents q_len_b <= 128. */
 typedef struct {
     gqa_tensor_t q, k, v;
     gqa_tensor_t attn_mask;
@@ -171,21 +182,40 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * on success.
  *
  * The kernel plan (and with it the workspace size) is chosen per call from
- * the shapes.  Three environment variables, read at each call, override it
- * for measurement: GQA_ATTN_DECODE_SPLIT (keys per decode split, a power of
- * two in 128..8192), GQA_ATTN_PREFILL_SPLITS (key slices of the prefill
- * split-KV path, 1..32) and GQA_ATTN_XCD_REMAP=0 (no XCD-aware workgroup
- * order).  Query the workspace size with the same environment as the
- * forward call. */
+ * the shapes.  Three environment variables, read once per process (at the
+ * first call), override it for measurement: GQA_ATTN_DECODE_SPLIT (keys per
+ * decode split, a power of two in 128..8192), GQA_ATTN_PREFILL_SPLITS (key
+ * slices of the prefill split-KV path, 1..32) and GQA_ATTN_XCD_REMAP=0 (no
+ * XCD-aware workgroup order). */
 int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 
 /* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
  * stream).  workspace: device memory of at least gqa_attn_workspace_size
  * bytes (may be NULL when that is 0), owned by the caller and not used by
  * any other in-flight call.  Returns GQA_OK once the kernels are enqueued;
- * a HIP launch error returns GQA_ERR_HIP (see gqa_attn_last_hip_error). */
+ * a HIP launch error returns GQA_ERR_HIP (see gqa_attn_last_hip_error).
+ *
+ * Debug mode: with GQA_ATTN_VALIDATE=1 in the environment (read once per
+ * process), each call first runs a one-workgroup kernel that checks the
+ * device-side length preconditions above on the device arrays, waits for it
+ * (the call then synchronizes `stream`, so it cannot be captured into a
+ * graph) and returns GQA_ERR_INVALID_ARG, naming the violated condition in
+ * gqa_attn_last_error, without launching any attention kernel.  The check
+ * writes its result to one word of device memory per device held by the
+ * library: calls that overlap on one device race on it. */
 int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/* The device-side length preconditions above, checked on the host over host
+ * copies of the call's length arrays (query_lengths_host, kv_lengths_host,
+ * kv_page_table_host: the same contents as args->query_lengths,
+ * args->kv_lengths and args->kv_page_table; each needed when that argument
+ * is non-NULL).  For callers that hold the lengths on the host anyway; the
+ * device check of GQA_ATTN_VALIDATE=1 evaluates the same predicate.  Also
+ * runs every host check of gqa_attn_validate.  Returns GQA_OK or
+ * GQA_ERR_INVALID_ARG (detail in gqa_attn_last_error); launches nothing. */
+int gqa_attn_check_lengths(const gqa_attn_args_t* args, const int32_t* query_lengths_host,
+                           const int32_t* kv_lengths_host, const int32_t* kv_page_table_host);
 
 /* Human-readable text of a status code (static storage). */
 const char* gqa_attn_status_str(int status);
@@ -199,7 +229,7 @@ int gqa_attn_last_hip_error(void);
 
 /* Library ABI version (bumped on any change of these declarations or of
  * those in gqa_kv_cache.h; 2 adds the KV-cache update, 3 tree_parents, 4 paged
- * KV). */
+ * KV, 5 gqa_attn_check_lengths and 128-draft trees). */
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from gqa_attention_ragged_amd import capi
@@ -30,7 +31,8 @@ def test_library_exports_every_declared_function():
     assert "gqa_kv_cache_update" in names and "gqa_kv_cache_update_validate" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 4
+    assert lib.gqa_attn_abi_version() == 5
+    assert "gqa_attn_check_lengths" in names
 
 
 _addr = [0x100000]
@@ -215,16 +217,17 @@ def test_kv_update_validate_rejects():
 
 
 def test_tree_parents_validation():
-    """Tree decoding resolves up to 64 drafts per sequence: padded Q with
-    N_q > 64 is rejected on the host; packed Q and N_q <= 64 pass."""
-    a = base_args(nq=64)
+    """Tree decoding resolves up to 128 drafts per sequence: padded Q with
+    N_q > 128 is rejected on the host; packed Q (checked on the device) and
+    N_q <= 128 pass."""
+    a = base_args(nq=128, nkv=140)
     a.tree_parents = 0x7200000
     assert st(a) == capi.GQA_OK, capi.last_error()
-    a = base_args(nq=65, nkv=80)
+    a = base_args(nq=129, nkv=140)
     a.tree_parents = 0x7200000
     assert st(a) == capi.GQA_ERR_UNSUPPORTED
     assert "tree_parents" in capi.last_error()
-    a = base_args(PACKED, PADDED, nq=100, nkv=120)
+    a = base_args(PACKED, PADDED, nq=200, nkv=220)
     a.tree_parents = 0x7200000
     assert st(a) == capi.GQA_OK, capi.last_error()
 
@@ -265,3 +268,126 @@ def test_paged_kv_validation():
     a = _paged_args()
     a.kv_form = 3
     assert st(a) == capi.GQA_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------------ 32-bit windows
+def test_negative_strides_rejected():
+    a = base_args()
+    a.k.stride[2] = -128
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+    assert "negative stride" in capi.last_error()
+    a = base_args()
+    a.attn_mask = fake([2, 1, 64, 80], BOOL, strides=[5120, 5120, -80, 1])
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+
+
+def test_window_spans_below_4gib():
+    """A key tile / decode split (8448 rows) and a query tile (32 rows) are
+    read through 32-bit windows with 64-bit bases: the row stride times that
+    many rows must stay below 4 GiB, however long the whole sequence is."""
+    # a 262144-token packed KV of 64 heads x 128 f16 spans 4 GiB per tensor
+    # but 8448 rows of it only 138 MB: accepted
+    a = base_args(PACKED, PACKED, B=1, hq=64, hkv=64, nq=262144, nkv=262144)
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    # a row stride of 512 KiB (f16: 262144 elements): 8448 rows reach 4 GiB
+    big = 262144
+    a = base_args(PADDED, PACKED, B=1, nkv=100)
+    a.k = fake([100, 2, 128], F16, strides=[big, 128, 1])
+    a.v = fake([100, 2, 128], F16, strides=[big, 128, 1])
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+    assert "4 GiB" in capi.last_error()
+    # just below: 8448 rows of 256 KiB stride minus a row: 2.2 GB, accepted
+    a.k = fake([100, 2, 128], F16, strides=[big // 2, 128, 1])
+    a.v = fake([100, 2, 128], F16, strides=[big // 2, 128, 1])
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    # Q: 32 rows of a 160 MiB stride
+    a = base_args()
+    q_stride = 80 << 20  # elements (f16): 160 MiB per row, 31 rows > 4 GiB
+    a.q = fake([2, 8, 64, 128], F16, strides=[64 * q_stride, 128, q_stride, 1])
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------- device-side preconditions
+def _lens_args(qf=PACKED, kf=PADDED, B=3, nq=50, nkv=80, mask=None, tree=False, paged=False):
+    a = base_args(qf, kf, B=B, nq=nq, nkv=nkv)
+    if qf == PADDED:
+        a.query_lengths = 0x7000000
+    if kf == PADDED:
+        a.kv_lengths = 0x7100000
+    if mask is not None:
+        a.attn_mask = fake(mask, BOOL)
+    if tree:
+        a.tree_parents = 0x7200000
+    if paged:
+        a.kv_form = 2
+        a.k = fake([12, 2, 64, 128], F16)
+        a.v = fake([12, 2, 64, 128], F16)
+        a.kv_page_table = 0x7300000
+        a.kv_max_pages = 2
+    return a
+
+
+def _chk(a, ql=None, kl=None, pt=None):
+    return capi.gqa_attn_check_lengths(a, ql, kl, pt)
+
+
+def test_check_lengths_accepts_valid():
+    a = _lens_args()                                  # packed Q (T = 150), padded KV [B]
+    assert _chk(a, [0, 50, 50, 150], [60, 0, 80]) == capi.GQA_OK, capi.last_error()
+    a = _lens_args(PACKED, PACKED)                    # both packed: T_kv = 240
+    assert _chk(a, [0, 1, 2, 3], [0, 100, 100, 240]) == capi.GQA_OK, capi.last_error()
+    a = _lens_args(PADDED, PADDED)                    # padded Q with lengths
+    assert _chk(a, [0, 50, 99, 100], [80, 1, 0]) == capi.GQA_OK, capi.last_error()
+
+
+@pytest.mark.parametrize("case,ql,kl,needle", [
+    ("ql0", [1, 50, 50, 150], [60, 0, 80], "query_lengths[0]"),
+    ("ql_order", [0, 50, 40, 150], [60, 0, 80], "non-decreasing"),
+    ("ql_range", [0, 50, 50, 151], [60, 0, 80], "exceed q"),
+    ("kl_neg", [0, 50, 50, 150], [60, -1, 80], "kv_lengths"),
+    ("kl_range", [0, 50, 50, 150], [60, 0, 81], "exceed k/v"),
+])
+def test_check_lengths_rejects(case, ql, kl, needle):
+    a = _lens_args()
+    assert _chk(a, ql, kl) == capi.GQA_ERR_INVALID_ARG, case
+    assert needle in capi.last_error(), (case, capi.last_error())
+
+
+def test_check_lengths_packed_kv_and_padded_q():
+    a = _lens_args(PACKED, PACKED)
+    assert _chk(a, [0, 1, 2, 3], [2, 100, 100, 240]) == capi.GQA_ERR_INVALID_ARG
+    assert _chk(a, [0, 1, 2, 3], [0, 100, 90, 240]) == capi.GQA_ERR_INVALID_ARG
+    assert _chk(a, [0, 1, 2, 3], [0, 100, 100, 241]) == capi.GQA_ERR_INVALID_ARG
+    a = _lens_args(PADDED, PADDED)
+    assert _chk(a, [0, 51, 60, 70], [1, 1, 1]) == capi.GQA_ERR_INVALID_ARG  # q_len 51 > N_q 50
+
+
+def test_check_lengths_mask_tree_pages():
+    a = _lens_args(mask=[3, 1, 40, 80])               # mask rows cover 40 queries only
+    assert _chk(a, [0, 40, 40, 80], [60, 0, 80]) == capi.GQA_OK, capi.last_error()
+    assert _chk(a, [0, 41, 41, 81], [60, 0, 80]) == capi.GQA_ERR_INVALID_ARG
+    assert "attn_mask" in capi.last_error()
+    a = _lens_args(mask=[1, 1, 1, 70])                # broadcast rows, 70 keys
+    assert _chk(a, [0, 41, 41, 81], [70, 0, 5]) == capi.GQA_OK, capi.last_error()
+    assert _chk(a, [0, 41, 41, 81], [71, 0, 5]) == capi.GQA_ERR_INVALID_ARG
+    a = _lens_args(B=2, nq=200, nkv=300, tree=True)   # 128 drafts resolved per sequence
+    assert _chk(a, [0, 128, 200], [130, 300]) == capi.GQA_OK, capi.last_error()
+    assert _chk(a, [0, 129, 200], [130, 300]) == capi.GQA_ERR_INVALID_ARG
+    assert "drafts" in capi.last_error()
+    a = _lens_args(B=2, nq=4, paged=True)             # pools of 12 pages
+    pt = np.array([[[0, 9], [11, 3]], [[5, 5], [0, 0]]], dtype=np.int32)
+    assert _chk(a, [0, 4, 8], [128, 64], pt) == capi.GQA_OK, capi.last_error()
+    assert _chk(a, [0, 4, 8], [129, 64], pt) == capi.GQA_ERR_INVALID_ARG   # beyond 2 pages
+    bad = pt.copy()
+    bad[1, 0, 0] = 12                                  # K page 12 of a 12-page pool
+    assert _chk(a, [0, 4, 8], [128, 64], bad) == capi.GQA_ERR_INVALID_ARG
+    assert "page" in capi.last_error()
+    bad = pt.copy()
+    bad[1, 1, 1] = -1                                  # unused entry (64 keys = 1 page): ignored
+    assert _chk(a, [0, 4, 8], [128, 64], bad) == capi.GQA_OK, capi.last_error()
+
+
+def test_check_lengths_needs_host_copies():
+    a = _lens_args()
+    assert _chk(a, None, [60, 0, 80]) == capi.GQA_ERR_INVALID_ARG
+    assert "host copy" in capi.last_error()

@@ -91,9 +91,8 @@ def test_tree_split_kv():
 
 
 def test_tree_long_packed_rows():
-    """Packed sequences longer than 64 drafts run (rows past the first 64 see
-    the context and themselves only, the documented limit); with a star tree
-    that limit does not change the result, so every row must match."""
+    """Packed sequences of up to 100 drafts with a star tree (every draft
+    hangs off the context): each row sees the context and itself."""
     c = _tree_case(3500, qf="packed_nhd", kf="packed_nhd", tree="star", qmax=100, B=2)
     parity.compare(c, parity.run_gpu(c))
 
