@@ -114,6 +114,8 @@ def load() -> ctypes.CDLL:
         lib.gqa_attn_last_hip_error.restype = ctypes.c_int
         lib.gqa_attn_abi_version.argtypes = []
         lib.gqa_attn_abi_version.restype = ctypes.c_int
+        lib.gqa_attn_forward_noalloc.argtypes = [P, ctypes.c_void_p]
+        lib.gqa_attn_forward_noalloc.restype = ctypes.c_int
         I32 = ctypes.POINTER(ctypes.c_int32)
         lib.gqa_attn_check_lengths.argtypes = [P, I32, I32, I32]
         lib.gqa_attn_check_lengths.restype = ctypes.c_int
@@ -224,6 +226,13 @@ def gqa_attn_forward(args: GqaArgs, workspace: Optional[torch.Tensor], stream) -
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().gqa_attn_forward(ctypes.byref(args), ws_ptr, ws_n, stream)
+    if st != GQA_OK:
+        raise GqaError(st, last_error())
+
+
+def gqa_attn_forward_noalloc(args: GqaArgs, stream) -> None:
+    """The forward call whose workspace is the library's static buffer."""
+    st = load().gqa_attn_forward_noalloc(ctypes.byref(args), stream)
     if st != GQA_OK:
         raise GqaError(st, last_error())
 

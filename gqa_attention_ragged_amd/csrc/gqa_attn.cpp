@@ -512,11 +512,12 @@ int gqa_attn_check_lengths(const gqa_attn_args_t* args, const int32_t* query_len
     return GQA_OK;
 }
 
-int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
-                     void* stream) {
-    Plan plan;
-    int st = plan_call(args, &plan);
-    if (st != GQA_OK) return st;
+namespace {
+
+// Launch a planned call with the given workspace (the caller's, or the
+// library's static one).
+int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
+                    size_t workspace_bytes, void* stream) {
     if (plan.kernel == K_NONE) return GQA_OK;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipSuccess;
@@ -562,6 +563,35 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
         return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     }
     return GQA_OK;
+}
+
+}  // namespace
+
+int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    Plan plan;
+    const int st = plan_call(args, &plan);
+    if (st != GQA_OK) return st;
+    return forward_planned(args, plan, workspace, workspace_bytes, stream);
+}
+
+int gqa_attn_forward_noalloc(const gqa_attn_args_t* args, void* stream) {
+    Plan plan;
+    const int st = plan_call(args, &plan);
+    if (st != GQA_OK) return st;
+    if (plan.workspace == 0) return forward_planned(args, plan, nullptr, 0, stream);
+    if (plan.workspace > gqa::kStaticScratchBytes)
+        return fail(GQA_ERR_WORKSPACE,
+                    "the call needs %zu bytes of workspace; the static scratch buffer holds %zu "
+                    "(use gqa_attn_forward with a caller workspace)",
+                    plan.workspace, gqa::kStaticScratchBytes);
+    void* scratch = nullptr;
+    const hipError_t e = gqa::static_scratch_ptr(&scratch);
+    if (e != hipSuccess) {
+        g_hip_err = (int)e;
+        return fail(GQA_ERR_HIP, "static scratch address: %s", hipGetErrorString(e));
+    }
+    return forward_planned(args, plan, scratch, gqa::kStaticScratchBytes, stream);
 }
 
 const char* gqa_attn_status_str(int status) {

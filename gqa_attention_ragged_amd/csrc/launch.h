@@ -33,6 +33,11 @@ hipError_t launch_length_check(const LenCheck& c, uint32_t* status, hipStream_t 
 // Device address of this device's status word for the length check.
 hipError_t length_status_ptr(uint32_t** out);
 
+// The fixed device workspace of gqa_attn_forward_noalloc: 128 MiB per
+// device (static_scratch.hip), and this device's address of it.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+hipError_t static_scratch_ptr(void** out);
+
 // KV-cache update (TRT_KVCacheUpdate, linear mode).  Element strides; the
 // row of (b, h, n) of the cache / output starts at base + b*sb + h*sh + n*sn
 // elements; the packed update row r of head h at base + r*sn + h*sh.

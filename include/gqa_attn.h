@@ -206,6 +206,19 @@ int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* gqa_attn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the split-KV partials live in a static
+ * device buffer of the library, 128 MiB per device (allocated when the
+ * library's code object is loaded on a device and held until the process
+ * ends).  Calls whose plan needs more workspace than that (see
+ * gqa_attn_workspace_size) return GQA_ERR_WORKSPACE before launching
+ * anything.  The call allocates and frees nothing.  Every call on one device
+ * shares that device's buffer: calls that overlap on one device (other
+ * streams, other threads) race on it and must be serialized by the caller.
+ * Same arguments, results and error codes as gqa_attn_forward otherwise. */
+int gqa_attn_forward_noalloc(const gqa_attn_args_t* args, void* stream);
+
 /* The device-side length preconditions above, checked on the host over host
  * copies of the call's length arrays (query_lengths_host, kv_lengths_host,
  * kv_page_table_host: the same contents as args->query_lengths,
