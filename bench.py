@@ -421,6 +421,102 @@ def write_traffic(cfg: str, fetch_dir: str, write_dir: str) -> dict:
     return out
 
 
+# Two counter passes per prefill workload (at most 8 SQ counters each).
+COUNTER_PASSES = (
+    ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU",
+     "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
+    ["SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_CMD_FIFO_FULL",
+     "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_SALU", "SQ_WAIT_INST_LDS"],
+)
+SIMDS = 256 * 4
+
+
+def write_counters(cfg: str, dirs: list) -> dict:
+    """profiles/counters_<kernel>_cfg<cfg>.md from the rocprofv3 --pmc runs of
+    --profile-pass in `dirs` (one per COUNTER_PASSES entry): the counters of
+    the dominant kernel's dispatch, per wave and per 64-key wave-tile."""
+    import csv
+    import glob
+    from gqa_attention_ragged_amd import synth
+    case = synth.make_config(cfg, device="cpu")
+    w = work_of(case)
+    want = kernel_name(case, w["kind"]).split("::")[1]
+    vals = {}
+    kernel = None
+    dur_ns = None
+    for d in dirs:
+        per = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if want not in r["Kernel_Name"]:
+                    continue
+                kernel = r["Kernel_Name"]
+                key = (r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                dur_ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for (name, _), v in per.items():
+            vals[name] = v  # one dispatch of the kernel per profile pass
+    D = case.q.shape[-1]
+    # wave-tiles: 32 query rows x 64 keys per wave, over the allowed pairs
+    # rounded to whole tiles is not known here: report per allowed 32x64 block
+    blocks = w.get("pairs", 0) / (32 * 64)
+    out = {"workload": cfg, "kernel": kernel, "counters": vals, "dispatch_ns": dur_ns}
+    # GRBM_GUI_ACTIVE as collected is the sum over the 8 XCDs
+    g = vals.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+    if g:
+        out["mfma_busy_frac"] = vals.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (g * SIMDS)
+        if dur_ns:
+            out["clock_ghz"] = g / dur_ns
+    if vals.get("SQ_WAVE_CYCLES"):
+        out["wait_frac"] = vals.get("SQ_WAIT_INST_ANY", 0.0) / vals["SQ_WAVE_CYCLES"]
+        out["valu_active_frac"] = vals.get("SQ_ACTIVE_INST_VALU", 0.0) / vals["SQ_WAVE_CYCLES"]
+    if blocks:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS",
+                  "SQ_INSTS_SALU"):
+            if k in vals:
+                out[f"{k}_per_32x64_block"] = vals[k] / blocks
+    cmds = [f"rocprofv3 --pmc {' '.join(p)} --output-format csv -d <dir{i}> -o run -- "
+            f"python3 bench.py --profile-pass --workload {cfg}" for i, p in enumerate(COUNTER_PASSES)]
+    short = want.split("_kernel")[0]
+    path = os.path.join(ROOT, "profiles", f"counters_{short}_cfg{cfg}.md")
+    lines = [f"# {want} counters, workload {cfg}", "",
+             f"Workload: {synth.DESCRIPTIONS[cfg]}.", "",
+             "Commands (one rocprofv3 --pmc pass each, from the repository root):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += [f"    python3 bench.py --write-counters <dir0> <dir1> --workload {cfg}", "",
+              f"Kernel: `{kernel}` (one dispatch per pass); kernel sources sha {kernel_sha(w['kind'])}.",
+              "", "| Counter | Value |", "|---|---|"]
+    for k in sorted(vals):
+        lines.append(f"| {k} | {vals[k]:.6g} |")
+    lines += ["", "Derived:", ""]
+    if dur_ns:
+        lines.append(f"- dispatch duration under the counters: {dur_ns / 1e3:.1f} us")
+    if "mfma_busy_frac" in out:
+        lines.append(f"- MFMA busy: {out['mfma_busy_frac']:.3f} of the kernel's cycles per SIMD "
+                     "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs))")
+    if "clock_ghz" in out:
+        lines.append(f"- shader clock during the dispatch: {out['clock_ghz']:.2f} GHz "
+                     "(GRBM_GUI_ACTIVE / 8 over the dispatch duration)")
+    if "wait_frac" in out:
+        lines.append(f"- waves waiting on s_waitcnt: {out['wait_frac']:.3f} of wave cycles; "
+                     f"issuing VALU: {out['valu_active_frac']:.3f}")
+    if blocks:
+        lines.append(f"- per 32-row x 64-key block of allowed pairs ({blocks:.0f} blocks):")
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+                  "SQ_INSTS_SALU"):
+            if f"{k}_per_32x64_block" in out:
+                lines.append(f"  - {k}: {out[k + '_per_32x64_block']:.1f}")
+    if vals.get("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"- LDS bank conflicts: {vals.get('SQ_LDS_BANK_CONFLICT', 0) / vals['SQ_LDS_IDX_ACTIVE']:.3f}"
+                     " of LDS-active cycles; command FIFO full: "
+                     f"{vals.get('SQ_LDS_CMD_FIFO_FULL', 0):.4g} cycles")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    out["path"] = path
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -435,9 +531,13 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--write-counters", nargs="+", metavar="PASS_DIR")
     a = ap.parse_args()
     if a.write_traffic:
         print(json.dumps(write_traffic(a.workload, *a.write_traffic)))
+        return 0
+    if a.write_counters:
+        print(json.dumps(write_counters(a.workload, a.write_counters), default=str))
         return 0
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {a.gpus} requested); the "

@@ -49,7 +49,7 @@ int elem_kind(int dt) {
 
 int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
 
-enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2 };
+enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2, K_PREFILL_PP = 3 };
 
 // Draft tokens per sequence the tree variants resolve.
 constexpr int kMaxTreeDrafts = 128;
@@ -61,6 +61,7 @@ struct EnvOverrides {
     int prefill_splits = 0;  // GQA_ATTN_PREFILL_SPLITS: prefill key slices (0 = planner's)
     bool xcd_remap = true;   // GQA_ATTN_XCD_REMAP=0 turns the XCD-aware order off
     bool validate = false;   // GQA_ATTN_VALIDATE=1: device-side length checks before launching
+    bool pingpong = false;   // GQA_ATTN_PINGPONG=1: the 8-wave ping-pong kernel where it applies
 };
 
 const EnvOverrides& env_overrides() {
@@ -77,6 +78,7 @@ const EnvOverrides& env_overrides() {
         if (const char* s = std::getenv("GQA_ATTN_XCD_REMAP"))
             if (std::atoi(s) == 0) e.xcd_remap = false;
         if (const char* s = std::getenv("GQA_ATTN_VALIDATE")) e.validate = std::atoi(s) != 0;
+        if (const char* s = std::getenv("GQA_ATTN_PINGPONG")) e.pingpong = std::atoi(s) != 0;
         return e;
     }();
     return env;
@@ -401,8 +403,14 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
         return GQA_OK;
     }
 
+    // The 8-wave ping-pong kernel (one workgroup per CU) takes 16-bit Q/K/V of
+    // one type with online softmax and no mask, tree or paging; the 4-wave
+    // kernel (two workgroups per CU) everything else.
+    const bool pp = env_overrides().pingpong && qdt != GQA_DT_FP8_E4M3 && kdt == qdt &&
+                    a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF && !m.data &&
+                    !a->tree_parents && !paged;
     const int hw = gcd((int)G, 4);
-    const int R = 32 * (4 / hw);
+    const int R = 32 * ((pp ? 8 : 4) / hw);
     p.heads_per_wg = hw;
     p.rows_per_wg = R;
     // Mask tiles shared by a workgroup's heads are staged through LDS when the
@@ -431,7 +439,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // turn; the prefill kernel remaps ids so that an XCD works through whole
     // head groups when they divide evenly (GQA_ATTN_XCD_REMAP=0 turns it off).
     p.xcds = plan->grid_y % 8 == 0 && env_overrides().xcd_remap ? 8 : 0;
-    plan->kernel = K_PREFILL;
+    plan->kernel = pp ? K_PREFILL_PP : K_PREFILL;
     plan->workspace = 0;
     p.n_splits = 1;
     p.split_keys = 0;
@@ -441,8 +449,9 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // for online softmax (Q/DQ needs the full row before quantizing).
     const int64_t wgs = (int64_t)plan->grid_x * plan->grid_y;
     const int64_t kv_tiles = (kv_max + 63) / 64;
-    // Concurrent workgroups: two 4-wave workgroups per CU (256 CUs).
-    const int64_t slots = 512;
+    // Concurrent workgroups: two 4-wave workgroups per CU (256 CUs), or one
+    // 8-wave ping-pong workgroup.
+    const int64_t slots = pp ? 256 : 512;
     // Splitting pays while the workgroups fill the GPU about once (the
     // longest row tile then sets the time); the fp32 partials cost
     // rows * H_q * S * (D + 2) * 4 bytes written and read again.  Measured
@@ -556,7 +565,10 @@ int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
             plan.p.part_o = (float*)w;
             plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * plan.part_bytes);
         }
-        e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
+        if (plan.kernel == K_PREFILL_PP)
+            e = gqa::launch_prefill_pp(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
+        else
+            e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
     }
     if (e != hipSuccess) {
         g_hip_err = (int)e;

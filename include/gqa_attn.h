@@ -185,8 +185,11 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * the shapes.  Three environment variables, read once per process (at the
  * first call), override it for measurement: GQA_ATTN_DECODE_SPLIT (keys per
  * decode split, a power of two in 128..8192), GQA_ATTN_PREFILL_SPLITS (key
- * slices of the prefill split-KV path, 1..32) and GQA_ATTN_XCD_REMAP=0 (no
- * XCD-aware workgroup order). */
+ * slices of the prefill split-KV path, 1..32), GQA_ATTN_XCD_REMAP=0 (no
+ * XCD-aware workgroup order) and GQA_ATTN_PINGPONG=1 (an experimental
+ * 8-wave ping-pong prefill kernel for plain 16-bit softmax prefill without
+ * mask, tree, paging or Q/DQ; slower than the default 4-wave kernel on
+ * gfx950 today, kept for measurement). */
 int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 
 /* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
