@@ -380,14 +380,14 @@ struct Prefill {
         for (int k = 0; k < C::KMAX; ++k) {
             const int j = wave + 4 * k;
             const int dst = 4 * (k + 1) <= C::NKD || j < C::NKD ? j * 1024 : SSTAGE;
-            buf_load_lds16(kr, stage + dst, c.koff[k]);
+            buf_load_lds16_async(kr, stage + dst, c.koff[k]);
         }
         if (!with_v) return;
 #pragma unroll
         for (int k = 0; k < C::VMAX; ++k) {
             const int j = wave + 4 * k;
             const int dst = 4 * (k + 1) <= C::NVD || j < C::NVD ? C::KBYTES + j * 1024 : SSTAGE;
-            buf_load_lds16(vr, stage + dst, c.voff[k]);
+            buf_load_lds16_async(vr, stage + dst, c.voff[k]);
         }
     }
 
@@ -413,9 +413,9 @@ struct Prefill {
         }
         const char* row0 = sK + lr * C::KROW;
         const char* row1 = sK + (32 + lr) * C::KROW;
+        if constexpr (C::FP8) {
 #pragma unroll
-        for (int ks = 0; ks < C::QSTEPS; ++ks) {
-            if constexpr (C::FP8) {
+            for (int ks = 0; ks < C::QSTEPS; ++ks) {
                 i32x8 a0, a1;
                 {
                     const u32x4 lo = *(const u32x4*)(row0 + ks * 64 + lg * 32);
@@ -431,25 +431,32 @@ struct Prefill {
                 }
                 s[0] = mfma32_fp8(a0, qreg[ks], s[0]);
                 s[1] = mfma32_fp8(a1, qreg[ks], s[1]);
-            } else {
-                const V8 a0 = *(const V8*)(row0 + (ks * 16 + lg * 8) * 2);
-                const V8 a1 = *(const V8*)(row1 + (ks * 16 + lg * 8) * 2);
-                s[0] = mfma32(a0, qreg[ks], s[0]);
-                s[1] = mfma32(a1, qreg[ks], s[1]);
             }
-        }
-        if constexpr (!C::FP8 && C::QSTEPS == 8) {
-            // Schedule: eight K operand reads in flight ahead of the MFMAs
-            // (the default schedule waited on each pair just before its
-            // MFMAs, exposing the LDS latency): 8 reads, then 2 MFMAs and 2
-            // reads four times, then the last 8 MFMAs.
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads
+        } else {
+            // Explicit software pipeline (the source order is the
+            // instruction order: sched_barrier keeps the scheduler from
+            // sinking each operand read to its MFMA, which exposed the LDS
+            // latency on every MFMA): the K operands of k-step ks + LA are
+            // read while k-step ks's two MFMAs run.
+            constexpr int KS = C::QSTEPS, LA = 2;
+            V8 ka[LA + 1][2];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int ks = 0; ks < LA; ++ks) {
+                ka[ks][0] = *(const V8*)(row0 + (ks * 16 + lg * 8) * 2);
+                ka[ks][1] = *(const V8*)(row1 + (ks * 16 + lg * 8) * 2);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + LA < KS) {
+                    const int n = ks + LA;
+                    ka[n % (LA + 1)][0] = *(const V8*)(row0 + (n * 16 + lg * 8) * 2);
+                    ka[n % (LA + 1)][1] = *(const V8*)(row1 + (n * 16 + lg * 8) * 2);
+                }
+                s[0] = mfma32(ka[ks % (LA + 1)][0], qreg[ks], s[0]);
+                s[1] = mfma32(ka[ks % (LA + 1)][1], qreg[ks], s[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
 
@@ -563,19 +570,26 @@ struct Prefill {
         return __builtin_bit_cast(V8, w);
     }
 
-    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile.
+    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile, as an explicit
+    // software pipeline (source order = instruction order): the P operands
+    // are converted first, then each V operand (two transpose reads) is read
+    // LA MFMAs ahead of its use.
     __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
-        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+        constexpr int DB = D / 32, NC = 4 * DB, LA = 3;
+        V8 b[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            V8 b;
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
+            for (int e = 0; e < 8; ++e) b[ks][e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
+        V8 va[LA + 1];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const V8 a = v_operand(sV, ks, db);
-                o[db] = mfma32(a, b, o[db]);
-            }
+        for (int i = 0; i < LA; ++i) va[i] = v_operand(sV, i / DB, i % DB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            if (i + LA < NC) va[(i + LA) % (LA + 1)] = v_operand(sV, (i + LA) / DB, (i + LA) % DB);
+            o[i % DB] = mfma32(va[i % (LA + 1)], b[i / DB], o[i % DB]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 

@@ -34,6 +34,24 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, char* l
 #endif
 }
 
+// The same copy issued as an instruction the compiler does not see as a
+// write to LDS.  With the builtin the compiler guards LDS reads against the
+// copies in flight itself, and for reads it cannot tell apart from the
+// copied range (the transpose reads carry no alias information) it waits for
+// every copy in flight -- including the ones issued for later tiles, which
+// serializes the copy latency into the loop.  With this form it inserts no
+// such wait: the caller must wait for the copy (s_waitcnt vmcnt) and make it
+// visible to the other waves (barrier) before any wave reads the bytes.  The
+// instruction has no register result; M0 carries the LDS address.
+__device__ __forceinline__ void buf_load_lds16_async(__amdgpu_buffer_rsrc_t r, char* lds,
+                                                     uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+    __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m)
+                     : "memory");
+#endif
+}
+
 typedef __fp16 lds_h4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 // LDS transpose reads (gfx950): within each group of 16 lanes,
 // ds_read_b64_tr_b16 gives lane 4q+c the 16-bit element c of lanes 4k+q
