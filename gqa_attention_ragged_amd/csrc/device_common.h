@@ -107,6 +107,28 @@ template <> struct Vec8<bf16> { typedef bf16x8 type; };
 __device__ __forceinline__ f16 to_t(float x, f16*) { return (f16)x; }
 __device__ __forceinline__ bf16 to_t(float x, bf16*) { return (bf16)x; }
 
+// acc[i] += v[2i] + v[2i+1] for the eight 16-bit values of an operand: one
+// dot-product instruction per pair against (1, 1) (the products are exact,
+// the sum is formed in fp32).
+__device__ __forceinline__ void add_pairs(const f16x8& v, float (&acc)[4]) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 one = {(f16)1.f, (f16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const h2 pr = {v[2 * i], v[2 * i + 1]};
+        acc[i] = __builtin_amdgcn_fdot2(pr, one, acc[i], false);
+    }
+}
+__device__ __forceinline__ void add_pairs(const bf16x8& v, float (&acc)[4]) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const b2 pr = {v[2 * i], v[2 * i + 1]};
+        acc[i] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[i], false);
+    }
+}
+
 // Round |x| <= 448 to the nearest E4M3FN code (ties to even).  The hardware
 // conversion rounds to nearest-even but does not saturate, so the input is
 // clamped to the format's range first (saturating reading of Q/DQ).

@@ -570,17 +570,20 @@ struct Prefill {
         return __builtin_bit_cast(V8, w);
     }
 
-    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile, as an explicit
-    // software pipeline (source order = instruction order): the P operands
-    // are converted first, then each V operand (two transpose reads) is read
-    // LA MFMAs ahead of its use.
-    __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
-        constexpr int DB = D / 32, NC = 4 * DB, LA = 3;
-        V8 b[4];
+    // P^T of one tile as the four 16-bit BMM2 B operands (one per 16-key
+    // k-step): lane (row, group g) holds keys ks*16 + (e/4)*8 + g*4 + e%4.
+    __device__ __forceinline__ static void p_operands(const f32x16 (&pv)[2], V8 (&b)[4]) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) b[ks][e] = to_t(pv[ks >> 1][(ks & 1) * 8 + e], (T16*)nullptr);
+    }
+
+    // 16-bit BMM2: O^T += V^T P^T over one 64-key tile, as an explicit
+    // software pipeline (source order = instruction order): each V operand
+    // (two transpose reads) is read LA MFMAs ahead of its use.
+    __device__ __forceinline__ static void bmm2_ops(const char* sV, const V8 (&b)[4], ORegs& o) {
+        constexpr int DB = D / 32, NC = 4 * DB, LA = 3;
         V8 va[LA + 1];
 #pragma unroll
         for (int i = 0; i < LA; ++i) va[i] = v_operand(sV, i / DB, i % DB);
@@ -591,6 +594,11 @@ struct Prefill {
             o[i % DB] = mfma32(va[i % (LA + 1)], b[i / DB], o[i % DB]);
             __builtin_amdgcn_sched_barrier(0);
         }
+    }
+    __device__ __forceinline__ static void bmm2_16(const char* sV, const f32x16 (&pv)[2], ORegs& o) {
+        V8 b[4];
+        p_operands(pv, b);
+        bmm2_ops(sV, b, o);
     }
 
     // "none" normalization keeps unbounded scores: split each into a 16-bit
@@ -757,16 +765,33 @@ struct Prefill {
                         }
                         const float m_use = m_run == -INFINITY ? 0.f : m_run;
                         float l4[4] = {0.f, 0.f, 0.f, 0.f};
+                        if constexpr (KIND == PASS_ONLINE && !C::FP8) {
+                            // P in the BMM2 operand type; the row sum adds
+                            // those rounded values (dot products with one),
+                            // so l normalizes exactly the P that BMM2 uses
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb)
+                            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const float e = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
-                                s[kb][r] = e;
-                                l4[r & 3] += e;
-                            }
-                        l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
-                        if (KIND == PASS_ONLINE) bmm2_16(stage + C::KBYTES, s, o);
+                                for (int r = 0; r < 16; ++r)
+                                    s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
+                            V8 pb[4];
+                            p_operands(s, pb);
+#pragma unroll
+                            for (int ks = 0; ks < 4; ++ks) add_pairs(pb[ks], l4);
+                            l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+                            bmm2_ops(stage + C::KBYTES, pb, o);
+                        } else {
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const float e = fast_exp2(__builtin_fmaf(s[kb][r], eff, -m_use));
+                                    s[kb][r] = e;
+                                    l4[r & 3] += e;
+                                }
+                            l_run += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+                            if (KIND == PASS_ONLINE) bmm2_16(stage + C::KBYTES, s, o);
+                        }
                     } else {
                         // reference max and sum known: P = exp2(s - m) / l,
                         // x = P / qscale = exp2(s - m) * inv = exp2(s - m')
