@@ -61,6 +61,11 @@ struct AttnParams {
     // page table [B, 2, ptab_pages] (K pages, then V pages, per sequence)
     const int32_t* ptab;
     int32_t ptab_pages, page_shift, kv_paged;
+    // persistent prefill: the work-item grid (row-tile positions x head
+    // groups; key slices = n_splits) and the per-XCD claim counters (16
+    // ints apart, zeroed before each launch)
+    int32_t grid_x, grid_y;
+    int32_t* sched;
 };
 
 // ---------------------------------------------------------------- lengths
@@ -236,6 +241,10 @@ __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off,
 }
 __device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2& v) {
     v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+}
+// 16-byte buffer store; a lane outside the descriptor's range writes nothing.
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const u32x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 // Bytes from a window's first row to the end of its row n-1 (0 if n <= 0),
 // for windows the host has bounded below 2^32 bytes (a key tile, a split, a

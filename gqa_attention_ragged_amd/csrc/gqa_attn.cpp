@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -49,10 +50,12 @@ int elem_kind(int dt) {
 
 int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
 
-enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2, K_PREFILL_PP = 3 };
+enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2, K_PREFILL_PP = 3, K_PREFILL_PERSIST = 4 };
 
 // Draft tokens per sequence the tree variants resolve.
 constexpr int kMaxTreeDrafts = 128;
+// Claim counters of the persistent prefill kernel at the head of its workspace.
+constexpr size_t kSchedBytes = gqa::kSchedInts * sizeof(int32_t);
 
 // Plan overrides for measurement, read from the environment once per
 // process (the first call) rather than on every call.
@@ -62,6 +65,7 @@ struct EnvOverrides {
     bool xcd_remap = true;   // GQA_ATTN_XCD_REMAP=0 turns the XCD-aware order off
     bool validate = false;   // GQA_ATTN_VALIDATE=1: device-side length checks before launching
     bool pingpong = false;   // GQA_ATTN_PINGPONG=1: the 8-wave ping-pong kernel where it applies
+    bool persist = false;    // GQA_ATTN_PERSIST=1: the persistent prefill kernel where it applies
 };
 
 const EnvOverrides& env_overrides() {
@@ -79,6 +83,7 @@ const EnvOverrides& env_overrides() {
             if (std::atoi(s) == 0) e.xcd_remap = false;
         if (const char* s = std::getenv("GQA_ATTN_VALIDATE")) e.validate = std::atoi(s) != 0;
         if (const char* s = std::getenv("GQA_ATTN_PINGPONG")) e.pingpong = std::atoi(s) != 0;
+        if (const char* s = std::getenv("GQA_ATTN_PERSIST")) e.persist = std::atoi(s) != 0;
         return e;
     }();
     return env;
@@ -406,9 +411,15 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // The 8-wave ping-pong kernel (one workgroup per CU) takes 16-bit Q/K/V of
     // one type with online softmax and no mask, tree or paging; the 4-wave
     // kernel (two workgroups per CU) everything else.
-    const bool pp = env_overrides().pingpong && qdt != GQA_DT_FP8_E4M3 && kdt == qdt &&
-                    a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF && !m.data &&
-                    !a->tree_parents && !paged;
+    const bool plain16 = qdt != GQA_DT_FP8_E4M3 && kdt == qdt && a->norm == GQA_NORM_SOFTMAX &&
+                         a->qdq == GQA_QDQ_OFF && !m.data && !a->tree_parents && !paged;
+    const bool pp = env_overrides().pingpong && plain16;
+    // The same plain case can run as a persistent kernel (two workgroups per
+    // CU working through the row tiles, each prefetching its next item's
+    // first K / V tile and Q rows during the current item's last tile):
+    // faster on short sequences, slower on long ones, so opt-in.
+    const bool persist = !pp && env_overrides().persist && plain16 && B <= 64 &&
+                         window_fits(a->out, qf, 32);
     const int hw = gcd((int)G, 4);
     const int R = 32 * ((pp ? 8 : 4) / hw);
     p.heads_per_wg = hw;
@@ -439,7 +450,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // turn; the prefill kernel remaps ids so that an XCD works through whole
     // head groups when they divide evenly (GQA_ATTN_XCD_REMAP=0 turns it off).
     p.xcds = plan->grid_y % 8 == 0 && env_overrides().xcd_remap ? 8 : 0;
-    plan->kernel = pp ? K_PREFILL_PP : K_PREFILL;
+    plan->kernel = pp ? K_PREFILL_PP : persist ? K_PREFILL_PERSIST : K_PREFILL;
     plan->workspace = 0;
     p.n_splits = 1;
     p.split_keys = 0;
@@ -484,6 +495,15 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     }
     // the remap linearizes the grid in 32-bit arithmetic
     if ((int64_t)plan->grid_x * plan->grid_y * p.n_splits > INT32_MAX) p.xcds = 0;
+    p.grid_x = plan->grid_x;
+    p.grid_y = plan->grid_y;
+    if (plan->kernel == K_PREFILL_PERSIST) {
+        // the claim counters lead the workspace (the split partials, if
+        // any, follow them)
+        if ((int64_t)plan->grid_x * plan->grid_y * std::max(p.n_splits, 1) > INT32_MAX)
+            return fail(GQA_ERR_UNSUPPORTED, "too many work items");
+        plan->workspace = kSchedBytes + (plan->workspace ? plan->workspace : 256);
+    }
     return GQA_OK;
 }
 
@@ -525,6 +545,20 @@ namespace {
 
 // Launch a planned call with the given workspace (the caller's, or the
 // library's static one).
+// Compute units of the current device (the persistent prefill grid is two
+// workgroups per CU); 256, MI355X's count, if the query fails.
+int device_cus() {
+    static std::atomic<int> cache[256];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 256;
+    int v = cache[dev].load();
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+        v = 256;
+    cache[dev].store(v);
+    return v;
+}
+
 int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
                     size_t workspace_bytes, void* stream) {
     if (plan.kernel == K_NONE) return GQA_OK;
@@ -555,17 +589,31 @@ int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
         plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * sizeof(float));
         e = gqa::launch_decode(plan.p, plan.q_elem, plan.kv_elem, plan.head_dim, s);
     } else {
-        if (plan.p.n_splits > 1) {
+        const bool persist = plan.kernel == K_PREFILL_PERSIST;
+        if (persist || plan.p.n_splits > 1) {
             if (!workspace || workspace_bytes < plan.workspace)
                 return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed", plan.workspace);
-            uintptr_t w = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+        }
+        uintptr_t w = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+        if (persist) {
+            plan.p.sched = (int32_t*)w;
+            w += kSchedBytes;
+        }
+        if (plan.p.n_splits > 1) {
             const int64_t rows = plan.p.q_packed ? args->q.shape[0]
                                                  : (int64_t)plan.p.batch * plan.p.n_q;
             const int64_t slots = rows * plan.p.hq * plan.p.n_splits;
             plan.p.part_o = (float*)w;
             plan.p.part_ml = (float*)(w + (size_t)slots * plan.head_dim * plan.part_bytes);
         }
-        if (plan.kernel == K_PREFILL_PP)
+        if (plan.kernel == K_PREFILL_PERSIST) {
+            // two workgroups per CU (at most one per work item); the XCD
+            // order needs a workgroup on every XCD
+            const int64_t items = (int64_t)plan.grid_x * plan.grid_y * std::max(plan.p.n_splits, 1);
+            const int wgs = (int)std::min<int64_t>(items, 2 * (int64_t)device_cus());
+            if (wgs < 8) plan.p.xcds = 0;
+            e = gqa::launch_prefill_persist(plan.p, plan.q_elem, plan.head_dim, wgs, s);
+        } else if (plan.kernel == K_PREFILL_PP)
             e = gqa::launch_prefill_pp(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
         else
             e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);

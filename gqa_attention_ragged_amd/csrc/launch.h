@@ -17,6 +17,12 @@ hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_
 // mask; grid_x row tiles of rows_per_wg rows) and its split-KV combine.
 hipError_t launch_prefill_pp(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
                              hipStream_t stream);
+// Persistent prefill (16-bit, online softmax, no mask / tree / paging):
+// zeroes p.sched (kSchedInts ints), then runs `workgroups` workgroups over
+// the grid_x x grid_y x n_splits work items of p.
+constexpr int kSchedInts = 8 * 16;
+hipError_t launch_prefill_persist(const AttnParams& p, int elem, int head_dim, int workgroups,
+                                  hipStream_t stream);
 
 // The general prefill kernels of one element type (launch_prefill's parts).
 hipError_t launch_prefill_f16(const AttnParams& p, int head_dim, int grid_x, int grid_y,

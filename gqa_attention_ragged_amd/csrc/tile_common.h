@@ -129,6 +129,59 @@ __device__ __forceinline__ SeqInfo map_lane_info(const AttnParams& p) {
     return si;
 }
 
+// Dispatch order of the sequences for the tile maps below (wave 0, at most
+// 64 sequences: lane l holds sequence l's `si`): lane j receives the j-th
+// sequence in dispatch order (`idx`, past the batch: an index >= batch),
+// its row-tile count `n` (R rows per tile) and the inclusive scan `incl` of
+// the counts in that order.
+__device__ __forceinline__ void dispatch_order(const AttnParams& p, int R, const SeqInfo& si,
+                                               int& idx, int& n, int& incl) {
+    const int lane = threadIdx.x & 63;
+    // Bitonic sort of the (KV length, index) pairs into dispatch
+    // order (longer first, then lower index; lanes past the batch
+    // sort last) over groups of NMAX = 16, 32 or 64 lanes, the
+    // smallest that holds the batch (groups past the first hold
+    // only empty lanes), then an inclusive scan of the row-tile
+    // counts in that order.
+    int key = si.kv_len;
+    idx = lane;
+    n = lane < p.batch ? (si.q_len + R - 1) / R : 0;  // row tiles
+    const int nmax = p.batch <= 16 ? 16 : p.batch <= 32 ? 32 : 64;
+    // one compare-exchange step with the partner lane ^ stride
+    auto step = [&](auto stride_c, int size) {
+        constexpr int stride = decltype(stride_c)::value;
+        const int pk = xor_lanes<stride>(key), pi = xor_lanes<stride>(idx);
+        const int pn = xor_lanes<stride>(n);
+        // does the partner's pair come first in dispatch order?
+        const bool pfirst = pk > key || (pk == key && pi < idx);
+        const bool lower = (lane & stride) == 0;
+        const bool fwd = size == nmax || (lane & size) == 0;  // run direction
+        if (pfirst == (lower == fwd)) {
+            key = pk;
+            idx = pi;
+            n = pn;
+        }
+    };
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S4 = std::integral_constant<int, 4>;
+    using S8 = std::integral_constant<int, 8>;
+    using S16 = std::integral_constant<int, 16>;
+    using S32 = std::integral_constant<int, 32>;
+    step(S1{}, 2);
+    step(S2{}, 4), step(S1{}, 4);
+    step(S4{}, 8), step(S2{}, 8), step(S1{}, 8);
+    step(S8{}, 16), step(S4{}, 16), step(S2{}, 16), step(S1{}, 16);
+    if (nmax >= 32) {
+        step(S16{}, 32), step(S8{}, 32), step(S4{}, 32), step(S2{}, 32), step(S1{}, 32);
+    }
+    if (nmax == 64) {
+        step(S32{}, 64), step(S16{}, 64), step(S8{}, 64), step(S4{}, 64), step(S2{}, 64);
+        step(S1{}, 64);
+    }
+    incl = wave_incl_scan(n);
+}
+
 // Dispatch position `pos` -> (b, row tile within b); sequence b has
 // ceil(q_len_b / R) row tiles.  Positions run over the sequences by
 // decreasing KV length (ties: lower index first; more than 64 sequences:
@@ -145,49 +198,8 @@ __device__ __forceinline__ void map_tile(const AttnParams& p, int pos, int R, in
     if (wave == 0) {
         if (lane == 0) s_map[0] = -1;
         if (p.batch <= 64) {
-            // Bitonic sort of the (KV length, index) pairs into dispatch
-            // order (longer first, then lower index; lanes past the batch
-            // sort last) over groups of NMAX = 16, 32 or 64 lanes, the
-            // smallest that holds the batch (groups past the first hold
-            // only empty lanes), then an inclusive scan of the row-tile
-            // counts in that order.
-            int key = si.kv_len;
-            int idx = lane;
-            int n = lane < p.batch ? (si.q_len + R - 1) / R : 0;  // row tiles
-            const int nmax = p.batch <= 16 ? 16 : p.batch <= 32 ? 32 : 64;
-            // one compare-exchange step with the partner lane ^ stride
-            auto step = [&](auto stride_c, int size) {
-                constexpr int stride = decltype(stride_c)::value;
-                const int pk = xor_lanes<stride>(key), pi = xor_lanes<stride>(idx);
-                const int pn = xor_lanes<stride>(n);
-                // does the partner's pair come first in dispatch order?
-                const bool pfirst = pk > key || (pk == key && pi < idx);
-                const bool lower = (lane & stride) == 0;
-                const bool fwd = size == nmax || (lane & size) == 0;  // run direction
-                if (pfirst == (lower == fwd)) {
-                    key = pk;
-                    idx = pi;
-                    n = pn;
-                }
-            };
-            using S1 = std::integral_constant<int, 1>;
-            using S2 = std::integral_constant<int, 2>;
-            using S4 = std::integral_constant<int, 4>;
-            using S8 = std::integral_constant<int, 8>;
-            using S16 = std::integral_constant<int, 16>;
-            using S32 = std::integral_constant<int, 32>;
-            step(S1{}, 2);
-            step(S2{}, 4), step(S1{}, 4);
-            step(S4{}, 8), step(S2{}, 8), step(S1{}, 8);
-            step(S8{}, 16), step(S4{}, 16), step(S2{}, 16), step(S1{}, 16);
-            if (nmax >= 32) {
-                step(S16{}, 32), step(S8{}, 32), step(S4{}, 32), step(S2{}, 32), step(S1{}, 32);
-            }
-            if (nmax == 64) {
-                step(S32{}, 64), step(S16{}, 64), step(S8{}, 64), step(S4{}, 64), step(S2{}, 64);
-                step(S1{}, 64);
-            }
-            const int incl = wave_incl_scan(n);
+            int idx, n, incl;
+            dispatch_order(p, R, si, idx, n, incl);
             const int ahead = incl - n;
             const uint64_t hit = __ballot(n > 0 && pos >= ahead && pos < incl);
             if (hit != 0 && __builtin_amdgcn_readlane(idx, (int)__builtin_ctzll(hit)) < p.batch) {

@@ -189,7 +189,11 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * XCD-aware workgroup order) and GQA_ATTN_PINGPONG=1 (an experimental
  * 8-wave ping-pong prefill kernel for plain 16-bit softmax prefill without
  * mask, tree, paging or Q/DQ; slower than the default 4-wave kernel on
- * gfx950 today, kept for measurement). */
+ * gfx950 today, kept for measurement) and GQA_ATTN_PERSIST=1 (a persistent
+ * form of the 4-wave kernel for the same plain case with at most 64
+ * sequences: two workgroups per CU claim row tiles in turn and prefetch the
+ * next one's first K / V tile and Q rows; faster on short sequences, slower
+ * on long ones; needs a workspace of its 512-byte claim counters). */
 int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 
 /* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
