@@ -414,23 +414,25 @@ struct Prefill {
         const char* row0 = sK + lr * C::KROW;
         const char* row1 = sK + (32 + lr) * C::KROW;
         if constexpr (C::FP8) {
+            // every K operand of the tile (one or two 64-byte k-steps per
+            // key block) read before the first MFMA, which then waits for
+            // its own reads only (sched_barrier keeps the order)
+            i32x8 a[C::QSTEPS][2];
+#pragma unroll
+            for (int ks = 0; ks < C::QSTEPS; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const char* row = kb ? row1 : row0;
+                    const u32x4 lo = *(const u32x4*)(row + ks * 64 + lg * 32);
+                    const u32x4 hi = *(const u32x4*)(row + ks * 64 + lg * 32 + 16);
+                    a[ks][kb][0] = lo[0]; a[ks][kb][1] = lo[1]; a[ks][kb][2] = lo[2]; a[ks][kb][3] = lo[3];
+                    a[ks][kb][4] = hi[0]; a[ks][kb][5] = hi[1]; a[ks][kb][6] = hi[2]; a[ks][kb][7] = hi[3];
+                }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                i32x8 a0, a1;
-                {
-                    const u32x4 lo = *(const u32x4*)(row0 + ks * 64 + lg * 32);
-                    const u32x4 hi = *(const u32x4*)(row0 + ks * 64 + lg * 32 + 16);
-                    a0[0] = lo[0]; a0[1] = lo[1]; a0[2] = lo[2]; a0[3] = lo[3];
-                    a0[4] = hi[0]; a0[5] = hi[1]; a0[6] = hi[2]; a0[7] = hi[3];
-                }
-                {
-                    const u32x4 lo = *(const u32x4*)(row1 + ks * 64 + lg * 32);
-                    const u32x4 hi = *(const u32x4*)(row1 + ks * 64 + lg * 32 + 16);
-                    a1[0] = lo[0]; a1[1] = lo[1]; a1[2] = lo[2]; a1[3] = lo[3];
-                    a1[4] = hi[0]; a1[5] = hi[1]; a1[6] = hi[2]; a1[7] = hi[3];
-                }
-                s[0] = mfma32_fp8(a0, qreg[ks], s[0]);
-                s[1] = mfma32_fp8(a1, qreg[ks], s[1]);
+                s[0] = mfma32_fp8(a[ks][0], qreg[ks], s[0]);
+                s[1] = mfma32_fp8(a[ks][1], qreg[ks], s[1]);
             }
         } else {
             // Explicit software pipeline (the source order is the
@@ -625,22 +627,35 @@ struct Prefill {
     }
 
     // fp8 BMM2: P' codes (E4M3FN) against V^T codes, one 64-key k-step.
+    // fp8 BMM2 A operand for d-block db: four 8-key transpose reads; read t
+    // holds keys key(t, g, k).
+    __device__ __forceinline__ static i32x8 v_operand_fp8(const char* sV, int db) {
+        const int lane = threadIdx.x & 63, lg = lane >> 5;
+        const int l16 = lane & 15, dh = (lane >> 4) & 1, k = l16 >> 1;
+        const int d = db * 32 + dh * 16 + 8 * (l16 & 1);
+        i32x8 a;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int key = (t >> 1) * 32 + ((t & 1) * 2 + (k >> 2)) * 8 + lg * 4 + (k & 3);
+            const u32x2 w = tr8(sV + v_addr<C>(key, d));
+            a[2 * t] = (int)w[0];
+            a[2 * t + 1] = (int)w[1];
+        }
+        return a;
+    }
+    // fp8 BMM2 over the tile's one 64-key k-step, each d-block's operand
+    // read LA MFMAs ahead of its use (source order = instruction order).
     __device__ __forceinline__ static void bmm2_fp8(const char* sV, const i32x8& codes, ORegs& o) {
-        const int lane = threadIdx.x & 63, lr = lane & 31, lg = lane >> 5;
+        constexpr int DB = D / 32, LA = DB > 2 ? 2 : 1;
+        i32x8 va[LA + 1];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            // four 8-key transpose reads; read t holds keys key(t, g, k)
-            const int l16 = lane & 15, dh = (lane >> 4) & 1, k = l16 >> 1;
-            const int d = db * 32 + dh * 16 + 8 * (l16 & 1);
-            i32x8 a;
+        for (int i = 0; i < LA; ++i) va[i] = v_operand_fp8(sV, i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int key = (t >> 1) * 32 + ((t & 1) * 2 + (k >> 2)) * 8 + lg * 4 + (k & 3);
-                const u32x2 w = tr8(sV + v_addr<C>(key, d));
-                a[2 * t] = (int)w[0];
-                a[2 * t + 1] = (int)w[1];
-            }
-            o[db] = mfma32_fp8(a, codes, o[db]);
+        for (int db = 0; db < DB; ++db) {
+            if (db + LA < DB) va[(db + LA) % (LA + 1)] = v_operand_fp8(sV, db + LA);
+            o[db] = mfma32_fp8(va[db % (LA + 1)], codes, o[db]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
