@@ -273,7 +273,14 @@ struct Prefill {
         const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
         const int64_t off = (int64_t)tile * (C::BN * es);
         const __amdgpu_buffer_rsrc_t mr = make_rsrc(c.mtile + off, clamp_range(c.mvalid - off));
-        buf_load(mr, c.moff, rm);
+        if (MACC && c.mbool) {
+            u32x2 v;  // fp8 kernels stage bool masks in 8-byte chunks
+            buf_load(mr, c.moff, v);
+            rm[0] = v[0];
+            rm[1] = v[1];
+        } else {
+            buf_load(mr, c.moff, rm);
+        }
     }
     // Staged rows hold 16-bit additive values; a bool chunk (16 keys) becomes
     // 16 f16 values, 0 (may attend) or -inf.  fp8 kernels (MACC) store fp32
@@ -284,13 +291,16 @@ struct Prefill {
         char* row = stage + C::STAGE + c.mrow_l * MROW;
         if constexpr (MACC) {
             if (c.mbool) {
+                // 8 keys: byte b -> bias (b - 1) & 0xFF800000, i.e. -inf for
+                // a zero byte and +0 for any other (b - 1 < 2^23)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
+                for (int w = 0; w < 2; ++w) {
                     const uint32_t x = rm[w];
                     f32x4 f;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) f[u] = ((x >> (8 * u)) & 0xffu) ? 0.f : -INFINITY;
-                    *(f32x4*)(row + c.mchunk * 64 + w * 16) = f;
+                    for (int u = 0; u < 4; ++u)
+                        f[u] = __builtin_bit_cast(float, (((x >> (8 * u)) & 0xffu) - 1u) & 0xFF800000u);
+                    *(f32x4*)(row + c.mchunk * 32 + w * 16) = f;
                 }
             } else {
 #pragma unroll
@@ -1031,10 +1041,13 @@ struct Prefill {
         c.mchunk = 0;
         c.mbool = p.mask_kind == MASK_BOOL;
         if constexpr (STAGED) {
-            // 32 rows x BN keys; bool: 4 chunks of 16 B per row (threads
-            // 0..127), 16-bit: 8 chunks per row (all 256 threads).
+            // 32 rows x BN keys; 16-bit: 8 chunks of 16 B per row (all 256
+            // threads); bool: 4 chunks of 16 B per row (threads 0..127),
+            // or in the fp8 kernels, whose staging expands each byte to four,
+            // 8 chunks of 8 B (all 256 threads)
             const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
-            const int cpr = C::BN * es / 16;
+            const int chunk = MACC && c.mbool ? 8 : 16;
+            const int cpr = C::BN * es / chunk;
             if (tid < 32 * cpr) {
                 c.mrow_l = tid / cpr;
                 c.mchunk = tid % cpr;
@@ -1047,7 +1060,7 @@ struct Prefill {
             // valid chunk would otherwise be range-checked out as zeros.
             const int64_t kend = ((int64_t)c.kv_len * es + 15) & ~(int64_t)15;
             c.mvalid = rows > 0 && c.kv_len > 0 ? (int64_t)(rows - 1) * p.m_si * es + kend : 0;
-            c.moff = c.mrow_l >= 0 ? (uint32_t)((int64_t)c.mrow_l * p.m_si * es + c.mchunk * 16)
+            c.moff = c.mrow_l >= 0 ? (uint32_t)((int64_t)c.mrow_l * p.m_si * es + c.mchunk * chunk)
                                    : 0xFFFFFFF0u;  // idle threads: out of range, no access
         }
         if (HAS_MASK) {
