@@ -431,6 +431,71 @@ COUNTER_PASSES = (
 SIMDS = 256 * 4
 
 
+def write_trace(cfg: str, trace_dir: str, steps: int = 50) -> dict:
+    """profiles/<kernel>_cfg<cfg>.md from a rocprofv3 --kernel-trace --stats run
+    of `bench.py --workload <cfg> --no-secondary --no-cpu`: the per-kernel
+    statistics (kernels above 0.5% of GPU time), the dominant kernel's average
+    over its last `steps` dispatches (the timed steps) and the algorithmic rate
+    that average gives, beside the rate bench.py reported in the same run."""
+    import csv
+    import glob
+    from gqa_attention_ragged_amd import synth
+    case = synth.make_config(cfg, device="cpu")
+    w = work_of(case)
+    want = kernel_name(case, w["kind"]).split("::")[1]
+    stats = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True):
+        stats += list(csv.DictReader(open(f)))
+    trace = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        trace += list(csv.DictReader(open(f)))
+    if not stats or not trace:
+        raise SystemExit(f"no kernel statistics or trace under {trace_dir}")
+    mine = [r for r in trace if want in r["Kernel_Name"]]
+    mine.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = mine[-steps:]
+    avg_ns = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in last) / len(last)
+    kernel = last[0]["Kernel_Name"]
+    if w["kind"] == "decode":
+        rate, unit, peak = w["bytes"] / avg_ns, "GB/s", HBM_PEAK
+        work = f"{w['bytes'] / 1e9:.3f} GB of K/V, Q and Y per step"
+    else:
+        rate, unit = w["flop"] / avg_ns / 1e3, "TFLOP/s"
+        peak = PEAK[dtype_name(case)]
+        work = f"{w['flop'] / 1e9:.2f} GFLOP per step"
+    # bench.py's own line, printed by the traced run
+    bench_line = None
+    for f in glob.glob(os.path.join(trace_dir, "..", f"trace_{cfg}.log")):
+        for line in open(f):
+            if line.startswith("{"):
+                bench_line = json.loads(line)
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- "
+           f"python3 bench.py --workload {cfg} --no-secondary --no-cpu")
+    short = want.replace("_kernel", "")
+    path = os.path.join(ROOT, "profiles", f"{short}_kernel_cfg{cfg}.md")
+    lines = [f"# {want}, workload {cfg}", "", f"Workload: {synth.DESCRIPTIONS[cfg]}.", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", f"    {cmd}",
+             f"    python3 bench.py --write-trace {trace_dir} --workload {cfg}", "",
+             f"Kernel sources sha {kernel_sha(w['kind'])}.  Kernel statistics (every dispatch of the run: "
+             "warm-up and timed steps; rows below 0.5% of GPU time omitted):", "",
+             "| kernel | calls | average ns | min ns | max ns | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["Percentage"])):
+        if float(r["Percentage"]) < 0.5:
+            continue
+        name = r["Name"] if len(r["Name"]) < 90 else r["Name"][:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"Average of the dominant kernel's last {len(last)} dispatches (the timed steps): "
+              f"{avg_ns:.0f} ns.", f"Algorithmic work {work} / {avg_ns / 1e3:.1f} us = {rate:.1f} {unit} "
+              f"({rate / peak:.3f} of the {peak:g} {unit} peak)."]
+    if bench_line:
+        lines.append(f"bench.py in the same run (HIP events over the timed steps, whole step): "
+                     f"{bench_line['value']} {bench_line['unit']}, {bench_line['ms_per_step']} ms/step.")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return {"workload": cfg, "kernel": kernel, "avg_ns": avg_ns, "rate": rate, "unit": unit, "path": path}
+
+
 def write_counters(cfg: str, dirs: list) -> dict:
     """profiles/counters_<kernel>_cfg<cfg>.md from the rocprofv3 --pmc runs of
     --profile-pass in `dirs` (one per COUNTER_PASSES entry): the counters of
@@ -532,12 +597,16 @@ def main() -> int:
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-counters", nargs="+", metavar="PASS_DIR")
+    ap.add_argument("--write-trace", metavar="TRACE_DIR")
     a = ap.parse_args()
     if a.write_traffic:
         print(json.dumps(write_traffic(a.workload, *a.write_traffic)))
         return 0
     if a.write_counters:
         print(json.dumps(write_counters(a.workload, a.write_counters), default=str))
+        return 0
+    if a.write_trace:
+        print(json.dumps(write_trace(a.workload, a.write_trace), default=str))
         return 0
     if a.gpus != 1:
         print(f"bench.py: this build measures one GPU only (--gpus {a.gpus} requested); the "
