@@ -21,7 +21,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "lib", "libgqa_attn.so")
 SOURCES = ["gqa_attn.cpp", "prefill.hip", "prefill_f16.hip", "prefill_bf16.hip", "prefill_fp8.hip",
-           "prefill_pp.hip", "prefill_persist.hip",
+           "prefill_kv8_f16.hip", "prefill_kv8_bf16.hip", "prefill_pp.hip",
+           "prefill_persist.hip",
            "decode.hip", "kv_cache.hip", "validate.hip", "static_scratch.hip"]
 ARCH = os.environ.get("GQA_ATTN_ARCH", "gfx950")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")

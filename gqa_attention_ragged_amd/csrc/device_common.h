@@ -66,6 +66,7 @@ struct AttnParams {
     // ints apart, zeroed before each launch)
     int32_t grid_x, grid_y;
     int32_t* sched;
+    int32_t kv8;                      // 1: fp8 E4M3FN K / V with 16-bit Q (prefill)
 };
 
 // ---------------------------------------------------------------- lengths

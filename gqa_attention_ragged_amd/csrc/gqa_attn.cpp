@@ -316,10 +316,12 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
                         a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
                         a->causal_kind != GQA_CAUSAL_UPPER_LEFT && G <= 16 &&
                         qdt != GQA_DT_FP8_E4M3;
-    if (kv_cache8 && !decode)
+    // an fp8 KV cache with 16-bit Q: the decode kernels, or the prefill kernels
+    // that convert each K / V tile to 16 bits in LDS (online softmax)
+    const bool kv8 = kv_cache8 && !decode;
+    if (kv8 && (a->norm != GQA_NORM_SOFTMAX || a->qdq != GQA_QDQ_OFF))
         return fail(GQA_ERR_UNSUPPORTED,
-                    "an fp8 KV cache with 16-bit Q is supported for the decode step "
-                    "(padded Q with N_q = 1, softmax, no mask, no Q/DQ, causal none/lower_right)");
+                    "an fp8 KV cache with 16-bit Q needs softmax without Q/DQ");
     if (paged && !decode &&
         (a->norm != GQA_NORM_SOFTMAX || a->qdq != GQA_QDQ_OFF || a->k.shape[2] < 64))
         return fail(GQA_ERR_UNSUPPORTED,
@@ -431,7 +433,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // 32 rows; with tree decoding a mask is read per lane (the generic
     // variant carries the tree rule).
     p.mask_lds = 0;
-    if (m.data && !a->tree_parents && !paged && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
+    if (m.data && !a->tree_parents && !paged && !kv8 && R == 32 && p.m_sh == 0 && p.m_sj == 1 &&
         (p.mask_kind == gqa::MASK_BOOL || p.mask_kind == gqa::MASK_F16 ||
          p.mask_kind == gqa::MASK_BF16)) {
         const int64_t es = p.mask_kind == gqa::MASK_BOOL ? 1 : 2;
@@ -497,6 +499,7 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     if ((int64_t)plan->grid_x * plan->grid_y * p.n_splits > INT32_MAX) p.xcds = 0;
     p.grid_x = plan->grid_x;
     p.grid_y = plan->grid_y;
+    p.kv8 = kv8;
     if (plan->kernel == K_PREFILL_PERSIST) {
         // the claim counters lead the workspace (the split partials, if
         // any, follow them)

@@ -31,6 +31,11 @@ hipError_t launch_prefill_bf16(const AttnParams& p, int head_dim, int grid_x, in
                                hipStream_t stream);
 hipError_t launch_prefill_fp8(const AttnParams& p, int head_dim, int grid_x, int grid_y,
                               hipStream_t stream);
+// 16-bit Q over an fp8 KV cache (p.kv8)
+hipError_t launch_prefill_kv8_f16(const AttnParams& p, int head_dim, int grid_x, int grid_y,
+                                  hipStream_t stream);
+hipError_t launch_prefill_kv8_bf16(const AttnParams& p, int head_dim, int grid_x, int grid_y,
+                                   hipStream_t stream);
 
 // Decode (query length 1) split-KV partial pass and its combine.
 // q_elem: Q type (f16/bf16); kv_elem: K/V type (same as q, or fp8).

@@ -156,7 +156,7 @@ constexpr int kWaitLgkmcnt0 = 0xC07F;
 // generic and tree variants (a tree with a mask takes the generic one).
 enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3, MK_TREE = 4 };
 
-template <typename TI, int D, int MK, bool PAGED = false>
+template <typename TI, int D, int MK, bool PAGED = false, bool KV8 = false>
 struct Prefill {
     static constexpr bool HAS_MASK = MK != MK_NONE && MK != MK_TREE;
     static constexpr bool TREE = MK == MK_GENERIC || MK == MK_TREE;  // tree rule compiled in
@@ -182,6 +182,17 @@ struct Prefill {
     // of range: zeros, no memory access) into a spare 1 KiB after the stage,
     // so that the copy has no wave-dependent branches.
     static constexpr int SPARE = (C::NKD % 4 || C::NVD % 4) ? 1024 : 0;
+    // fp8 KV cache with 16-bit Q (KV8): K / V tiles are copied as E4M3FN codes
+    // in unpadded rows of D bytes into small stages (an even number of 1 KiB
+    // copies per wave: no spare) and converted once per tile, by the whole
+    // workgroup, into the 16-bit tile (`t16`, layout of a 16-bit stage) that
+    // the products read.  E4M3FN values are exact in f16 and bf16.
+    static_assert(!KV8 || !C::FP8, "KV8: 16-bit Q");
+    static constexpr int KES = KV8 ? 1 : C::ES;  // K / V bytes per element in memory
+    static constexpr int K8BYTES = C::BN * D, V8BYTES = C::BN * D;
+    static constexpr int STAGE8 = K8BYTES + V8BYTES;
+    static constexpr int K8PW = K8BYTES / 4096, V8PW = V8BYTES / 4096;  // copies per wave
+    static_assert(K8BYTES % 4096 == 0 && K8PW <= C::KMAX && V8PW <= C::VMAX, "KV8 copies");
     // Q / O tiles staged through LDS, row-major with XOR-swizzled 16-byte
     // chunks (chunk c of row r at c ^ (r mod chunks per row)) so that the
     // 32 rows of an operand read spread over the banks.  Each wave stages
@@ -375,30 +386,63 @@ struct Prefill {
             const int row0 = tile * C::BN;
             const int pi = row0 >> p.page_shift;
             const int within = row0 & ((1 << p.page_shift) - 1);
-            const uint32_t valid = rows_bytes(min(C::BN, c.kv_len - row0), p.k.sn, D, C::ES);
+            const uint32_t valid = rows_bytes(min(C::BN, c.kv_len - row0), p.k.sn, D, KES);
             const int32_t* pt = p.ptab + (int64_t)c.b * 2 * p.ptab_pages + pi;
-            kr = make_rsrc(c.kbase + ((int64_t)pt[0] * p.k.sb + (int64_t)within * p.k.sn) * C::ES,
+            kr = make_rsrc(c.kbase + ((int64_t)pt[0] * p.k.sb + (int64_t)within * p.k.sn) * KES,
                            valid);
             vr = make_rsrc(c.vbase + ((int64_t)pt[p.ptab_pages] * p.v.sb +
-                                      (int64_t)within * p.v.sn) * C::ES,
-                           rows_bytes(min(C::BN, c.kv_len - row0), p.v.sn, D, C::ES));
+                                      (int64_t)within * p.v.sn) * KES,
+                           rows_bytes(min(C::BN, c.kv_len - row0), p.v.sn, D, KES));
         } else {
             kr = window(c.kbase, c.kbytes, c.ktile, tile);
             vr = window(c.vbase, c.vbytes, c.vtile, tile);
+        }
+        if constexpr (KV8) {
+#pragma unroll
+            for (int k = 0; k < K8PW; ++k)
+                buf_load_lds16_async<PAGED>(kr, stage + (wave + 4 * k) * 1024, c.koff[k]);
+            if (!with_v) return;
+#pragma unroll
+            for (int k = 0; k < V8PW; ++k)
+                buf_load_lds16_async<PAGED>(vr, stage + K8BYTES + (wave + 4 * k) * 1024, c.voff[k]);
+            return;
         }
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) {
             const int j = wave + 4 * k;
             const int dst = 4 * (k + 1) <= C::NKD || j < C::NKD ? j * 1024 : SSTAGE;
-            buf_load_lds16_async(kr, stage + dst, c.koff[k]);
+            buf_load_lds16_async<PAGED>(kr, stage + dst, c.koff[k]);
         }
         if (!with_v) return;
 #pragma unroll
         for (int k = 0; k < C::VMAX; ++k) {
             const int j = wave + 4 * k;
             const int dst = 4 * (k + 1) <= C::NVD || j < C::NVD ? C::KBYTES + j * 1024 : SSTAGE;
-            buf_load_lds16_async(vr, stage + dst, c.voff[k]);
+            buf_load_lds16_async<PAGED>(vr, stage + dst, c.voff[k]);
         }
+    }
+
+    // KV8: the fp8 tile in `s8` (K then V, rows of D codes) into the 16-bit
+    // tile `t16` (K rows padded, V rows with XOR-swizzled 16-byte units, as a
+    // 16-bit stage): every thread converts 8-code chunks of whole rows.
+    __device__ __forceinline__ static void convert_tile(const char* s8, char* t16) {
+        constexpr int CPR = D / 8, NCH = C::BN * CPR;
+        static_assert(NCH % 256 == 0, "chunks divide over the workgroup");
+#pragma unroll
+        for (int k = 0; k < NCH / 256; ++k) {
+            const int i = (int)threadIdx.x + 256 * k, row = i / CPR, c8 = i % CPR;
+            const u32x2 kw = *(const u32x2*)(s8 + row * D + c8 * 8);
+            const u32x2 vw = *(const u32x2*)(s8 + K8BYTES + row * D + c8 * 8);
+            *(V8*)(t16 + row * C::KROW + c8 * 16) = e4m3x8_to<T16>(kw);
+            *(V8*)(t16 + C::KBYTES + row * C::VROW + ((c8 ^ v_swz<C>(row)) << 4)) = e4m3x8_to<T16>(vw);
+        }
+    }
+    // Workgroup barrier after LDS writes that leaves the tile copies in flight.
+    __device__ __forceinline__ static void lds_barrier() {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
     }
 
     // S^T tile (64 keys x 32 rows) for this wave from the staged K tile.  The
@@ -694,7 +738,8 @@ struct Prefill {
                                                  char* __restrict__ st0, char* __restrict__ st1,
                                                  const QRegs& qreg, float sc, float ac,
                                                  float& m_run, float& l_run, float inv, ORegs& o,
-                                                 const u32x4& rm0 = u32x4{}) {
+                                                 const u32x4& rm0 = u32x4{},
+                                                 char* __restrict__ t16 = nullptr) {
         const bool with_v = KIND != PASS_STATS;
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
         const float kadd = ac / sc;  // staged mask weight on raw scores
@@ -714,10 +759,17 @@ struct Prefill {
         // Loop body for tile `it` computed from `stage` while tile it+1 is
         // staged into `nstage`; unrolled by two below so that both stage
         // addresses are compile-time LDS offsets.
-        auto body = [&](int it, char* __restrict__ stage, char* __restrict__ nstage) {
+        auto body = [&](int it, char* __restrict__ stage_in, char* __restrict__ nstage) {
             const bool more = it + 1 < c.t1;
             if (more) dma_tile(p, c, it + 1, with_v, nstage, wave);
             if (mlds && more) load_mask(p, c, it + 1, rm);
+            // KV8: the products read the 16-bit tile converted from this
+            // tile's codes (the previous tile's barrier freed it)
+            char* const stage = KV8 ? t16 : stage_in;
+            if constexpr (KV8) {
+                convert_tile(stage_in, t16);
+                lds_barrier();
+            }
             const int j0 = it * C::BN;
             if (c.wave_rows && j0 < c.wave_kv_end) {
                 f32x16 s[2];
@@ -861,7 +913,8 @@ struct Prefill {
 
     template <int MODE>
     __device__ __forceinline__ static void run(const AttnParams& p, char* __restrict__ st0,
-                                               char* __restrict__ st1) {
+                                               char* __restrict__ st1,
+                                               char* __restrict__ t16 = nullptr) {
         __shared__ int s_map[6];
         const int tid = threadIdx.x, lane = tid & 63;
         // wave index in a scalar register: everything derived from it is
@@ -1006,13 +1059,26 @@ struct Prefill {
                             : p.kv_packed ? (int64_t)kv_start * p.k.sn : (int64_t)b * p.k.sb;
         const int64_t vro = PAGED ? 0
                             : p.kv_packed ? (int64_t)kv_start * p.v.sn : (int64_t)b * p.v.sb;
-        c.kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * C::ES;
-        c.vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * C::ES;
-        c.kbytes = rows_bytes64(c.kv_len, p.k.sn, D, C::ES);
-        c.vbytes = rows_bytes64(c.kv_len, p.v.sn, D, C::ES);
-        c.ktile = (int64_t)C::BN * p.k.sn * C::ES;
-        c.vtile = (int64_t)C::BN * p.v.sn * C::ES;
-        {
+        c.kbase = (const char*)p.k.ptr + (kro + (int64_t)kvh * p.k.sh) * KES;
+        c.vbase = (const char*)p.v.ptr + (vro + (int64_t)kvh * p.v.sh) * KES;
+        c.kbytes = rows_bytes64(c.kv_len, p.k.sn, D, KES);
+        c.vbytes = rows_bytes64(c.kv_len, p.v.sn, D, KES);
+        c.ktile = (int64_t)C::BN * p.k.sn * KES;
+        c.vtile = (int64_t)C::BN * p.v.sn * KES;
+        if constexpr (KV8) {
+            // source of the 16 bytes this lane writes in each copy: rows of
+            // D codes, unpadded, in both tiles
+#pragma unroll
+            for (int k = 0; k < C::KMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                c.koff[k] = k < K8PW ? (uint32_t)((int64_t)(pos / D) * p.k.sn + pos % D) : 0xFFFFFFF0u;
+            }
+#pragma unroll
+            for (int k = 0; k < C::VMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                c.voff[k] = k < V8PW ? (uint32_t)((int64_t)(pos / D) * p.v.sn + pos % D) : 0xFFFFFFF0u;
+            }
+        } else {
             // source of the 16 LDS bytes this lane writes in each copy
             // instruction: K rows are padded (positions in the pad read as
             // zeros), V rows are swizzled (position -> logical 16-byte unit)
@@ -1084,7 +1150,7 @@ struct Prefill {
         // 1 KiB of whole rows, then read in operand layout.
         QRegs qreg;
         {
-            char* qs = st1 + wave * 32 * C::QROW;
+            char* qs = (KV8 ? t16 : st1) + wave * 32 * C::QROW;  // KV8: the free 16-bit tile
             const int nrows = max(0, min(32, c.q_len - c.wr0));
             const __amdgpu_buffer_rsrc_t qr = make_rsrc(
                 (const char*)p.q.ptr +
@@ -1174,7 +1240,8 @@ struct Prefill {
             poison_over(c, o);
             factor *= p.qscale;
         } else {
-            sweep<PASS_ONLINE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0);
+            sweep<PASS_ONLINE, true, true>(p, c, st0, st1, qreg, sc, ac, m_run, l_run, 0.f, o, rm0,
+                                           t16);
             poison_over(c, o);
             const float l_tot = halves_sum(l_run);
             if (nsl > 1) {
@@ -1208,7 +1275,8 @@ struct Prefill {
         // its slice of the stages (free after the key loop's last barrier)
         // so that every store writes 1 KiB of whole rows.
         {
-            char* os = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * C::OROW;
+            char* os = KV8 ? t16 + wave * 32 * C::OROW
+                           : (wave < 2 ? st0 : st1) + (wave & 1) * 32 * C::OROW;
             typedef TO TO4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
@@ -1253,6 +1321,19 @@ __global__ __launch_bounds__(256, (kPrefillWgsPerCu<TI, D, MODE>)) void prefill_
     __shared__ __attribute__((aligned(16))) char st0[P::SSTAGE + P::SPARE];
     __shared__ __attribute__((aligned(16))) char st1[P::SSTAGE + P::SPARE];
     P::template run<MODE>(p, st0, st1);
+}
+
+// fp8 KV cache with 16-bit Q: online softmax; fp8 stages for the copies and
+// one 16-bit tile for the products (and the Q / O staging).
+template <typename TI, int D, int MK, bool PAGED>
+__global__ __launch_bounds__(256, 2) void prefill_kv8_kernel(AttnParams p) {
+    typedef Prefill<TI, D, MK, PAGED, true> P;
+    static_assert(4 * 32 * P::C::QROW <= P::C::STAGE && 4 * 32 * P::C::OROW <= P::C::STAGE,
+                  "Q / O staging fits the 16-bit tile");
+    __shared__ __attribute__((aligned(16))) char st0[P::STAGE8];
+    __shared__ __attribute__((aligned(16))) char st1[P::STAGE8];
+    __shared__ __attribute__((aligned(16))) char t16[P::C::STAGE];
+    P::template run<MODE_SOFTMAX>(p, st0, st1, t16);
 }
 
 // Split-KV combine: one workgroup per (row tile, query head) merges the
@@ -1351,6 +1432,34 @@ static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t st
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS_BF16>), grid, dim3(256), 0, stream, p);
     else
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS16>), grid, dim3(256), 0, stream, p);
+}
+
+// fp8 KV cache with 16-bit Q (online softmax; masks read per lane), then the
+// split-KV merge when the keys are split.
+template <typename TI, int D>
+static hipError_t launch_kv8_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
+    if (p.kv_paged) {
+        if (p.mask_kind != MASK_NONE)
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_GENERIC, true>), grid, dim3(256), 0, stream, p);
+        else if (p.tree)
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_TREE, true>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_NONE, true>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (p.mask_kind != MASK_NONE)
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_GENERIC, false>), grid, dim3(256), 0, stream, p);
+        else if (p.tree)
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_TREE, false>), grid, dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_NONE, false>), grid, dim3(256), 0, stream, p);
+    }
+    if (p.n_splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((prefill_combine_kernel<TI, D>), dim3(grid_x, p.hq), dim3(256), 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 template <typename TI, int D>

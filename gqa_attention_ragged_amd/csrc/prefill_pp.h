@@ -76,7 +76,7 @@ struct PingPong {
             const int row = pos / C::KROW, byte = pos % C::KROW;
             const uint32_t off =
                 pos < C::KBYTES && byte < D * C::ES ? (uint32_t)row * cp.kstride + byte : 0xFFFFFFF0u;
-            buf_load_lds16_async(kr, stage + dst, off);
+            buf_load_lds16_async<true>(kr, stage + dst, off);
         }
 #pragma unroll
         for (int k = 0; k < VM; ++k) {
@@ -87,7 +87,7 @@ struct PingPong {
             const uint32_t off = pos < C::VBYTES
                                      ? (uint32_t)row * cp.vstride + ((unit ^ v_swz<C>(row)) << 4)
                                      : 0xFFFFFFF0u;
-            buf_load_lds16_async(vr, stage + dst, off);
+            buf_load_lds16_async<true>(vr, stage + dst, off);
         }
     }
 

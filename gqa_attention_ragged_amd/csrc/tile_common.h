@@ -43,12 +43,32 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, char* l
 // such wait: the caller must wait for the copy (s_waitcnt vmcnt) and make it
 // visible to the other waves (barrier) before any wave reads the bytes.  The
 // instruction has no register result; M0 carries the LDS address.
+//
+// The compiler does not check hazards into an asm block either, so the
+// block opens with the wait states the instruction needs itself: an LDS DMA
+// needs 1 after an SALU write of M0 (the compiler sets M0 right before the
+// block), and a VMEM instruction reading an SGPR that a VALU instruction
+// wrote needs 5.  VALU_RSRC: the descriptor's SGPRs may come from VALU
+// instructions (v_readfirstlane when a page table supplies the base,
+// v_readlane when they were spilled): s_nop 4 (5 wait states); otherwise
+// s_nop 0.  Without them the load can take the previous contents of a
+// descriptor SGPR as its base address.  The choice per kernel is checked on
+// the compiled code (every copy, the wait states back to the last VALU write
+// of its SGPRs and the last write of M0).
+template <bool VALU_RSRC>
 __device__ __forceinline__ void buf_load_lds16_async(__amdgpu_buffer_rsrc_t r, char* lds,
                                                      uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
     const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-    __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(r), "{m0}"(m)
-                     : "memory");
+    if constexpr (VALU_RSRC) {
+        __asm__ volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+                         "s"(r), "{m0}"(m)
+                         : "memory");
+    } else {
+        __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff),
+                         "s"(r), "{m0}"(m)
+                         : "memory");
+    }
 #endif
 }
 

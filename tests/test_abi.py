@@ -133,9 +133,15 @@ def test_head_size_and_dtype_support():
     assert st(a) == capi.GQA_OK, capi.last_error()
     a.qscale = 0.0
     assert st(a) == capi.GQA_ERR_INVALID_ARG
-    # fp8 KV cache with f16 Q: decode step only
-    assert st(base_args(kvdt=FP8)) == capi.GQA_ERR_UNSUPPORTED
+    # fp8 KV cache with f16 Q: decode and prefill with softmax, no Q/DQ
+    assert st(base_args(kvdt=FP8)) == capi.GQA_OK, capi.last_error()
     assert st(base_args(nq=1, kvdt=FP8)) == capi.GQA_OK, capi.last_error()
+    a = base_args(kvdt=FP8)
+    a.qdq, a.qscale = 1, 1 / 448
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
+    a = base_args(kvdt=FP8)
+    a.norm = 1  # "none"
+    assert st(a) == capi.GQA_ERR_UNSUPPORTED
 
 
 def test_mask_validation():
@@ -273,6 +279,19 @@ def test_paged_kv_validation():
     a = _paged_args()
     a.kv_form = 3
     assert st(a) == capi.GQA_ERR_INVALID_ARG
+    # fp8 KV in pages: prefill (with a mask or a tree too) and decode
+    a = _paged_args(nq=64)
+    a.k.dtype = a.v.dtype = FP8
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a.attn_mask = fake([2, 1, 64, 8 * 64], BOOL)
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a = _paged_args(nq=64)
+    a.k.dtype = a.v.dtype = FP8
+    a.tree_parents = 0x7200000
+    assert st(a) == capi.GQA_OK, capi.last_error()
+    a = _paged_args(nq=1)
+    a.k.dtype = a.v.dtype = FP8
+    assert st(a) == capi.GQA_OK, capi.last_error()
 
 
 # ------------------------------------------------------------ 32-bit windows
