@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -67,7 +68,14 @@ struct AttnParams {
     int32_t grid_x, grid_y;
     int32_t* sched;
     int32_t kv8;                      // 1: fp8 E4M3FN K / V with 16-bit Q (prefill)
+    // prefill: one record of kWorkRecInts per workgroup of the attention
+    // grid (linear id x + nx (y + ny z)), written by the plan kernel before
+    // the launch: sequence (-1: nothing to do), row tile, q_len, kv_len,
+    // q_start, kv_start, first head of the workgroup's head group, and
+    // kv head | key slice << 16.  Null: every workgroup builds its own map.
+    const int32_t* wrec;
 };
+constexpr int kWorkRecInts = 8;
 
 // ---------------------------------------------------------------- lengths
 __device__ __forceinline__ int q_len_of(const AttnParams& p, int b) {

@@ -54,6 +54,9 @@ enum Kernel { K_NONE = 0, K_PREFILL = 1, K_DECODE = 2, K_PREFILL_PP = 3, K_PREFI
 
 // Draft tokens per sequence the tree variants resolve.
 constexpr int kMaxTreeDrafts = 128;
+// Prefill grids of at least this many workgroups read their tile map from
+// records written by the plan kernel (see plan_call).
+constexpr int64_t kMinRecordWgs = 1024;
 // Claim counters of the persistent prefill kernel at the head of its workspace.
 constexpr size_t kSchedBytes = gqa::kSchedInts * sizeof(int32_t);
 
@@ -96,6 +99,7 @@ struct Plan {
     int grid_x = 0, grid_y = 0;
     size_t workspace = 0;
     size_t part_bytes = 4;  // prefill split-KV: bytes per partial O element
+    size_t rec_bytes = 0;   // prefill: per-workgroup records at the workspace's head
     gqa::LenCheck lc{};     // the call's device-side length preconditions
 };
 
@@ -500,6 +504,19 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     p.grid_x = plan->grid_x;
     p.grid_y = plan->grid_y;
     p.kv8 = kv8;
+    // The 4-wave kernel with at most 64 sequences reads its tile map from
+    // per-workgroup records that a plan kernel writes once per call (the
+    // sort and remap that every workgroup would otherwise repeat: about 1.9
+    // of a workgroup's 5.3 us outside the key loop); they lead the
+    // workspace.  Worth the extra launch (about 1.6 us) from two rounds of
+    // workgroups on: measured 64 x 256 tokens +7.2%, 64 x 512 +4.2%, 64 x
+    // 128 +2.7%, the ragged causal prefill +0.8%; a 6-workgroup call -18%.
+    const int64_t n_wg = (int64_t)plan->grid_x * plan->grid_y * std::max(p.n_splits, 1);
+    if (plan->kernel == K_PREFILL && B <= 64 && n_wg >= kMinRecordWgs) {
+        plan->rec_bytes =
+            ((size_t)n_wg * gqa::kWorkRecInts * sizeof(int32_t) + 255) & ~(size_t)255;
+        plan->workspace = plan->rec_bytes + (plan->workspace ? plan->workspace : 256);
+    }
     if (plan->kernel == K_PREFILL_PERSIST) {
         // the claim counters lead the workspace (the split partials, if
         // any, follow them)
@@ -598,6 +615,14 @@ int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
                 return fail(GQA_ERR_WORKSPACE, "workspace of %zu bytes needed", plan.workspace);
         }
         uintptr_t w = ((uintptr_t)workspace + 255) & ~(uintptr_t)255;
+        // the per-workgroup records need the whole workspace; without one a
+        // call without split-KV runs with the map built in every workgroup
+        const bool recs = plan.rec_bytes && workspace && workspace_bytes >= plan.workspace;
+        plan.p.wrec = nullptr;
+        if (recs) {
+            plan.p.wrec = (const int32_t*)w;
+            w += plan.rec_bytes;
+        }
         if (persist) {
             plan.p.sched = (int32_t*)w;
             w += kSchedBytes;
@@ -618,8 +643,15 @@ int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
             e = gqa::launch_prefill_persist(plan.p, plan.q_elem, plan.head_dim, wgs, s);
         } else if (plan.kernel == K_PREFILL_PP)
             e = gqa::launch_prefill_pp(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
-        else
-            e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x, plan.grid_y, s);
+        else {
+            if (recs) {
+                const int n_wg = plan.grid_x * plan.grid_y * std::max(plan.p.n_splits, 1);
+                e = gqa::launch_prefill_plan(plan.p, (int32_t*)plan.p.wrec, n_wg, s);
+            }
+            if (e == hipSuccess)
+                e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x,
+                                        plan.grid_y, s);
+        }
     }
     if (e != hipSuccess) {
         g_hip_err = (int)e;

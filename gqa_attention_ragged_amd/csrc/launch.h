@@ -13,6 +13,11 @@ enum Elem { ELEM_F16 = 0, ELEM_BF16 = 1, ELEM_FP8 = 2 };
 hipError_t launch_prefill(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,
                           hipStream_t stream);
 
+// Per-workgroup records of a prefill launch (AttnParams::wrec, kWorkRecInts
+// ints each) for the n_wg = grid_x * grid_y * max(n_splits, 1) workgroups of
+// launch_prefill's grid; p.batch <= 64.
+hipError_t launch_prefill_plan(const AttnParams& p, int32_t* rec, int n_wg, hipStream_t stream);
+
 // The 8-wave ping-pong prefill kernel (16-bit Q/K/V, online softmax, no
 // mask; grid_x row tiles of rows_per_wg rows) and its split-KV combine.
 hipError_t launch_prefill_pp(const AttnParams& p, int elem, int head_dim, int grid_x, int grid_y,

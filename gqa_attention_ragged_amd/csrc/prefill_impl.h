@@ -911,6 +911,46 @@ struct Prefill {
         if (it < c.t1) body(it, st0, st1);
     }
 
+    // Source offsets of the 16 bytes this lane writes in each tile-copy
+    // instruction (they depend on the lane and the row strides only).
+    __device__ __forceinline__ static void set_copy_offsets(const AttnParams& p, Ctx& c, int wave,
+                                                            int lane) {
+        if constexpr (KV8) {
+            // source of the 16 bytes this lane writes in each copy: rows of
+            // D codes, unpadded, in both tiles
+#pragma unroll
+            for (int k = 0; k < C::KMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                c.koff[k] = k < K8PW ? (uint32_t)((int64_t)(pos / D) * p.k.sn + pos % D) : 0xFFFFFFF0u;
+            }
+#pragma unroll
+            for (int k = 0; k < C::VMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                c.voff[k] = k < V8PW ? (uint32_t)((int64_t)(pos / D) * p.v.sn + pos % D) : 0xFFFFFFF0u;
+            }
+        } else {
+            // source of the 16 LDS bytes this lane writes in each copy
+            // instruction: K rows are padded (positions in the pad read as
+            // zeros), V rows are swizzled (position -> logical 16-byte unit)
+#pragma unroll
+            for (int k = 0; k < C::KMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                const int row = pos / C::KROW, byte = pos % C::KROW;
+                c.koff[k] = pos < C::KBYTES && byte < D * C::ES
+                                ? (uint32_t)((int64_t)row * p.k.sn * C::ES + byte)
+                                : 0xFFFFFFF0u;
+            }
+#pragma unroll
+            for (int k = 0; k < C::VMAX; ++k) {
+                const int pos = (wave + 4 * k) * 1024 + lane * 16;
+                const int row = pos / C::VROW, unit = (pos % C::VROW) / 16;
+                c.voff[k] = pos < C::VBYTES
+                                ? (uint32_t)((int64_t)row * p.v.sn * C::ES + ((unit ^ v_swz<C>(row)) << 4))
+                                : 0xFFFFFFF0u;
+            }
+        }
+    }
+
     template <int MODE>
     __device__ __forceinline__ static void run(const AttnParams& p, char* __restrict__ st0,
                                                char* __restrict__ st1,
@@ -922,47 +962,64 @@ struct Prefill {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int lr = lane & 31, lg = lane >> 5;
         const int R = p.rows_per_wg;
-        const SeqInfo si = map_lane_info(p);  // loads in flight during the remap
-        int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-        if (p.xcds > 1) {
-            // Consecutive workgroup ids go to the XCDs in turn (id % xcds),
-            // each with its own L2.  Remapped, XCD x takes one contiguous
-            // block of the work items ordered (head group, split, row tile),
-            // so the K/V rows of a head group are fetched into one L2 rather
-            // than into all of them.
-            const int nx = gridDim.x, ny = gridDim.y, nz = gridDim.z, X = p.xcds;
-            const int n = nx * ny * nz, L = bx + nx * (by + ny * bz);
-            const int xcd = L % X, k = L / X, q = n / X, r = n % X;
-            const int li = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + k;
-            bx = li % nx;
-            bz = (li / nx) % nz;
-            by = li / (nx * nz);
+        // This workgroup's record, when the plan kernel wrote them: the loads
+        // are issued first and the lane offsets below computed while they
+        // are in flight.
+        i32x4 rec0 = {-1, 0, 0, 0}, rec1 = {0, 0, 0, 0};
+        if (p.wrec) {
+            const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+            const i32x4* rp = (const i32x4*)(p.wrec + (int64_t)L * kWorkRecInts);
+            rec0 = rp[0];
+            rec1 = rp[1];
         }
-        // dispatch position -> (sequence, row tile), heaviest first
-        map_tile(p, bx, R, s_map, si);
-        // (b, row tile) are workgroup-uniform: read them into scalar registers
-        // so that every address and buffer descriptor built from them is
-        // scalar too (a descriptor in vector registers needs a loop per load).
-        const int b = __builtin_amdgcn_readfirstlane(s_map[0]);
-        if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
-
         Ctx c;
+        set_copy_offsets(p, c, wave, lane);
+        int b, tile, q_start, kv_start, hbase, kvh, bz;
+        if (p.wrec) {
+            // (b, row tile, ...) are workgroup-uniform: read into scalar
+            // registers, so every address and buffer descriptor built from
+            // them is scalar too (a descriptor in vector registers needs a
+            // loop per load)
+            b = __builtin_amdgcn_readfirstlane(rec0[0]);
+            if (b < 0) return;  // beyond the last tile of the batch (grid is an upper bound)
+            tile = __builtin_amdgcn_readfirstlane(rec0[1]);
+            c.q_len = __builtin_amdgcn_readfirstlane(rec0[2]);
+            c.kv_len = __builtin_amdgcn_readfirstlane(rec0[3]);
+            q_start = __builtin_amdgcn_readfirstlane(rec1[0]);
+            kv_start = __builtin_amdgcn_readfirstlane(rec1[1]);
+            hbase = __builtin_amdgcn_readfirstlane(rec1[2]);
+            const int kz = __builtin_amdgcn_readfirstlane(rec1[3]);
+            kvh = kz & 0xFFFF;
+            bz = kz >> 16;
+        } else {
+            const SeqInfo si = map_lane_info(p);  // loads in flight during the remap
+            int bx = blockIdx.x, by = blockIdx.y;
+            bz = blockIdx.z;
+            if (p.xcds > 1) xcd_remap(p.xcds, gridDim.x, gridDim.y, gridDim.z, bx, by, bz);
+            // dispatch position -> (sequence, row tile), heaviest first
+            map_tile(p, bx, R, s_map, si);
+            b = __builtin_amdgcn_readfirstlane(s_map[0]);
+            if (b < 0) return;
+            tile = __builtin_amdgcn_readfirstlane(s_map[1]);
+            c.q_len = __builtin_amdgcn_readfirstlane(s_map[2]);
+            c.kv_len = __builtin_amdgcn_readfirstlane(s_map[3]);
+            q_start = __builtin_amdgcn_readfirstlane(s_map[4]);
+            kv_start = __builtin_amdgcn_readfirstlane(s_map[5]);
+            hbase = by * p.heads_per_wg;
+            kvh = hbase / p.group;
+        }
         c.b = b;
-        c.q_len = __builtin_amdgcn_readfirstlane(s_map[2]);
-        c.kv_len = __builtin_amdgcn_readfirstlane(s_map[3]);
-        const int q_start = __builtin_amdgcn_readfirstlane(s_map[4]);
-        const int kv_start = __builtin_amdgcn_readfirstlane(s_map[5]);
         c.diag = p.causal == 1 ? 0 : c.kv_len - c.q_len;
         c.causal = p.causal != 0;
         c.tree = TREE && p.tree != nullptr;
         c.tbase = c.kv_len - c.q_len;
         c.anc0 = c.anc1 = c.anc2 = c.anc3 = 0u;
         c.tree_over = false;
-        const int row0 = __builtin_amdgcn_readfirstlane(s_map[1]) * R;
-        const int hw = p.heads_per_wg;
-        const int h = by * hw + (wave % hw);
-        const int kvh = (by * hw) / p.group;
-        c.wr0 = row0 + (wave / hw) * 32;
+        const int row0 = tile * R;
+        // heads per workgroup: 1, 2 or 4 (a power of two)
+        const int hw = p.heads_per_wg, hsh = __builtin_ctz((unsigned)hw);
+        const int h = hbase + (wave & (hw - 1));
+        c.wr0 = row0 + (wave >> hsh) * 32;
         c.i = c.wr0 + lr;
         c.wave_rows = c.wr0 < c.q_len;
         if (TREE && c.tree) {
@@ -1065,40 +1122,6 @@ struct Prefill {
         c.vbytes = rows_bytes64(c.kv_len, p.v.sn, D, KES);
         c.ktile = (int64_t)C::BN * p.k.sn * KES;
         c.vtile = (int64_t)C::BN * p.v.sn * KES;
-        if constexpr (KV8) {
-            // source of the 16 bytes this lane writes in each copy: rows of
-            // D codes, unpadded, in both tiles
-#pragma unroll
-            for (int k = 0; k < C::KMAX; ++k) {
-                const int pos = (wave + 4 * k) * 1024 + lane * 16;
-                c.koff[k] = k < K8PW ? (uint32_t)((int64_t)(pos / D) * p.k.sn + pos % D) : 0xFFFFFFF0u;
-            }
-#pragma unroll
-            for (int k = 0; k < C::VMAX; ++k) {
-                const int pos = (wave + 4 * k) * 1024 + lane * 16;
-                c.voff[k] = k < V8PW ? (uint32_t)((int64_t)(pos / D) * p.v.sn + pos % D) : 0xFFFFFFF0u;
-            }
-        } else {
-            // source of the 16 LDS bytes this lane writes in each copy
-            // instruction: K rows are padded (positions in the pad read as
-            // zeros), V rows are swizzled (position -> logical 16-byte unit)
-#pragma unroll
-            for (int k = 0; k < C::KMAX; ++k) {
-                const int pos = (wave + 4 * k) * 1024 + lane * 16;
-                const int row = pos / C::KROW, byte = pos % C::KROW;
-                c.koff[k] = pos < C::KBYTES && byte < D * C::ES
-                                ? (uint32_t)((int64_t)row * p.k.sn * C::ES + byte)
-                                : 0xFFFFFFF0u;
-            }
-#pragma unroll
-            for (int k = 0; k < C::VMAX; ++k) {
-                const int pos = (wave + 4 * k) * 1024 + lane * 16;
-                const int row = pos / C::VROW, unit = (pos % C::VROW) / 16;
-                c.voff[k] = pos < C::VBYTES
-                                ? (uint32_t)((int64_t)row * p.v.sn * C::ES + ((unit ^ v_swz<C>(row)) << 4))
-                                : 0xFFFFFFF0u;
-            }
-        }
         c.mrow = nullptr;
         c.mtile = nullptr;
         c.mvalid = 0;

@@ -202,6 +202,21 @@ __device__ __forceinline__ void dispatch_order(const AttnParams& p, int R, const
     incl = wave_incl_scan(n);
 }
 
+// XCD-aware remap of a workgroup's grid position (bx, by, bz) over X XCDs.
+// Consecutive workgroup ids go to the XCDs in turn (id % X), each with its
+// own L2; remapped, XCD x takes one contiguous block of the work items
+// ordered (head group, split, row tile), so the K / V rows of a head group
+// are fetched into one L2 rather than into all of them.
+__device__ __forceinline__ void xcd_remap(int X, int nx, int ny, int nz, int& bx, int& by,
+                                          int& bz) {
+    const int n = nx * ny * nz, L = bx + nx * (by + ny * bz);
+    const int xcd = L % X, k = L / X, q = n / X, r = n % X;
+    const int li = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + k;
+    bx = li % nx;
+    bz = (li / nx) % nz;
+    by = li / (nx * nz);
+}
+
 // Dispatch position `pos` -> (b, row tile within b); sequence b has
 // ceil(q_len_b / R) row tiles.  Positions run over the sequences by
 // decreasing KV length (ties: lower index first; more than 64 sequences:

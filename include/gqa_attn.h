@@ -181,6 +181,14 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * selected kernels need none).  Returns a gqa_status_t; *bytes is written
  * on success.
  *
+ * What it holds: the decode step's split-KV partials; for prefill with at
+ * most 64 sequences and a grid of at least 1024 workgroups, 32 bytes per
+ * workgroup (the tile map, computed once per call by a small plan kernel
+ * rather than in every workgroup), followed by the split-KV partials when
+ * the keys are split.  A prefill call without split-KV also runs when given no (or too
+ * little) workspace: each workgroup then builds the map itself (the same
+ * map, so the same results; slower).
+ *
  * The kernel plan (and with it the workspace size) is chosen per call from
  * the shapes.  Three environment variables, read once per process (at the
  * first call), override it for measurement: GQA_ATTN_DECODE_SPLIT (keys per
@@ -215,7 +223,8 @@ int gqa_attn_forward(const gqa_attn_args_t* args, void* workspace, size_t worksp
 
 /* gqa_attn_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation): the split-KV partials live in a static
+ * harnesses that forbid allocation): the workspace (tile-map records and
+ * split-KV partials) lives in a static
  * device buffer of the library, 128 MiB per device (allocated when the
  * library's code object is loaded on a device and held until the process
  * ends).  Calls whose plan needs more workspace than that (see

@@ -3,6 +3,7 @@ function include/gqa_attn.h declares, and its host-only entry points
 (validate, workspace_size, status strings) behave as documented.  No call
 here touches device memory: descriptors carry fake, aligned pointers."""
 import ctypes
+import math
 import os
 import re
 
@@ -161,13 +162,24 @@ def test_mask_validation():
 
 
 def test_workspace_sizes():
-    # prefill needs none (the opt-in persistent kernel: its claim counters,
+    # prefill: the per-workgroup records of the tile map, 32 bytes per
+    # workgroup (the opt-in persistent kernel: its claim counters instead,
     # under 1 KiB); the decode step (N_q = 1) needs split partials
     n0 = capi.gqa_attn_workspace_size(base_args())
-    assert n0 == 0 or (os.environ.get("GQA_ATTN_PERSIST") == "1" and n0 <= 1024)
+    if os.environ.get("GQA_ATTN_PERSIST") == "1":
+        assert 0 < n0 <= 1024
+    else:
+        assert n0 == 0  # 8 workgroups: each builds the map itself
     m = base_args()
     m.attn_mask = fake([2, 1, 64, 80], BOOL)
     assert capi.gqa_attn_workspace_size(m) == 0
+    # 64 x 512 rows x 8 head groups = 8192 workgroups: records
+    big = base_args(B=64, hq=32, hkv=8, nq=512)
+    big.attn_mask = fake([64, 1, 512, 80], BOOL)
+    n_wg = 64 * (512 // 32) * (32 // math.gcd(32 // 8, 4))
+    assert capi.gqa_attn_workspace_size(big) == (n_wg * 32 + 255) // 256 * 256 + 256
+    # more than 64 sequences: the workgroups build the map themselves
+    assert capi.gqa_attn_workspace_size(base_args(B=65, hq=32, hkv=8, nq=512)) == 0
     a = base_args(B=128, hq=32, hkv=8, nq=1, nkv=32768)
     n = capi.gqa_attn_workspace_size(a)
     assert n > 128 * 32 * 130 * 4

@@ -16,7 +16,10 @@ not valid), plus exact pins that need no oracle:
     Guide", AttentionPlugin: tree decoding; its INT4 GEMM section speaks of
     draft trees of 64 to 128 tokens), and NaN rows past the 128th draft;
   * split-KV outputs of |O| ~ 8 (f16 at D = 64 and 128);
-  * the GQA_ATTN_VALIDATE=1 device-side length check.
+  * the GQA_ATTN_VALIDATE=1 device-side length check;
+  * the tile map read from per-workgroup records (written by the plan kernel
+    into the workspace) against the map each workgroup builds itself (no
+    workspace): bitwise equal outputs, and equal to the oracle.
 """
 import dataclasses
 import itertools
@@ -263,3 +266,55 @@ def test_validate_mode_rejects_before_launch():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
     assert "validate ok" in r.stdout
+
+
+# ------------------------------------------------------ tile-map records
+def _run_ws(c, with_workspace):
+    out = synth.sentinel_like(c.q.shape, c.out_dtype, DEV)
+    args = capi.make_args(c.q, c.k, c.v, c.mask, out, **c.kwargs())
+    n = capi.gqa_attn_workspace_size(args)
+    assert n > 0  # the records are planned
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV) if with_workspace else None
+    capi.gqa_attn_forward(args, ws, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("hq,hkv,causal,qf,dtype", [
+    (16, 4, "lower_right", "packed_nhd", torch.float16),    # 4 head groups (no XCD remap)
+    (32, 8, "lower_right", "packed_nhd", torch.bfloat16),   # 8 head groups: XCD remap
+    (32, 8, "none", "padded_bhnd", torch.float16),
+    (12, 4, "upper_left", "padded_bhnd", torch.bfloat16),   # groups of 3: one head per workgroup
+])
+def test_records_equal_in_kernel_map(hq, hkv, causal, qf, dtype):
+    # at least 1024 workgroups, so that the call plans records
+    rng = np.random.default_rng(7700 + hq + hkv)
+    B = 64
+    ql = rng.integers(0, 400, size=B)
+    # at most 448 keys: no split-KV, so the call also runs without a workspace
+    kl = ql + rng.integers(0, 40, size=B) if causal == "lower_right" else rng.integers(1, 440, size=B)
+    n_q = int(ql.max()) + 3
+    c = synth.generate(seed=7700 + hq, q_lens=ql, kv_lens=kl, num_heads=hq, kv_num_heads=hkv,
+                       head_dim=128, query_form=qf, kv_form="padded_bhnd", dtype=dtype, n_q=n_q,
+                       n_kv=int(kl.max()) + 5, pass_query_lengths=True, causal_kind=causal,
+                       device=DEV, name=f"records-{hq}-{hkv}-{causal}-{qf}")
+    a = _run_ws(c, True)
+    b = _run_ws(c, False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    parity.compare(c, a)
+
+
+def test_records_with_split_kv():
+    # few rows over long keys, 8 head groups: about 128 workgroups split into
+    # about 12 key slices (over 1024 workgroups), so records and split
+    # partials share the workspace
+    rng = np.random.default_rng(7750)
+    ql = rng.integers(1, 60, size=8)
+    kl = ql + rng.integers(3000, 6000, size=8)
+    c = synth.generate(seed=7750, q_lens=ql, kv_lens=kl, num_heads=32, kv_num_heads=8,
+                       head_dim=128, query_form="packed_nhd", kv_form="padded_bhnd",
+                       dtype=torch.bfloat16, n_kv=int(kl.max()) + 3, causal_kind="lower_right",
+                       device=DEV, name="records-split")
+    args = capi.make_args(c.q, c.k, c.v, c.mask, torch.empty_like(c.q), **c.kwargs())
+    assert capi.gqa_attn_workspace_size(args) > int(ql.sum()) * 32 * 2 * 128 * 4
+    parity.compare(c, parity.run_gpu(c))
