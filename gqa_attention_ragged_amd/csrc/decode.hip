@@ -303,22 +303,45 @@ struct Decode {
         };
 
         // Software pipeline over this wave's tiles: the loads of the next tile
-        // are always issued before the current one is computed (past the
-        // split's end they fall outside the buffer range: zeros, no traffic).
+        // (16-bit KV) or the next two (fp8 KV) are always issued before the
+        // current one is computed (past the split's end they fall outside the
+        // buffer range: zeros, no traffic).
         const int stride = 4 * KT;
         int j0 = k0 + wave * KT;
         if (j0 < k1) {
-            Tile a, bt;
-            load(a, j0);
-            while (true) {
+            if constexpr (KV8) {
+                // an fp8 tile holds half the bytes of a 16-bit one: the loads
+                // of the next two tiles are in flight while one is computed
+                Tile a, bt, ct;
+                load(a, j0);
                 load(bt, j0 + stride);
-                compute(a, j0);
-                j0 += stride;
-                if (j0 >= k1) break;
-                load(a, j0 + stride);
-                compute(bt, j0);
-                j0 += stride;
-                if (j0 >= k1) break;
+                while (true) {
+                    load(ct, j0 + 2 * stride);
+                    compute(a, j0);
+                    j0 += stride;
+                    if (j0 >= k1) break;
+                    load(a, j0 + 2 * stride);
+                    compute(bt, j0);
+                    j0 += stride;
+                    if (j0 >= k1) break;
+                    load(bt, j0 + 2 * stride);
+                    compute(ct, j0);
+                    j0 += stride;
+                    if (j0 >= k1) break;
+                }
+            } else {
+                Tile a, bt;
+                load(a, j0);
+                while (true) {
+                    load(bt, j0 + stride);
+                    compute(a, j0);
+                    j0 += stride;
+                    if (j0 >= k1) break;
+                    load(a, j0 + stride);
+                    compute(bt, j0);
+                    j0 += stride;
+                    if (j0 >= k1) break;
+                }
             }
         }
 

@@ -229,8 +229,8 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     if (!window_fits(a->q, qf, 32))
         return fail(GQA_ERR_UNSUPPORTED, "q: 32 rows span 4 GiB or more (row stride too large)");
     // key windows: a 64-key tile (prefill), a split of up to 8192 keys plus
-    // the next tile's prefetch (decode)
-    const int64_t kv_window = 8192 + 256;
+    // the prefetch of up to two tiles of the 4 waves past its end (decode)
+    const int64_t kv_window = 8192 + 512;
     if (!window_fits(a->k, kf, kv_window) || !window_fits(a->v, kf, kv_window))
         return fail(GQA_ERR_UNSUPPORTED, "k/v: %lld rows span 4 GiB or more (row stride too large)",
                     (long long)kv_window);

@@ -137,7 +137,7 @@ typedef struct {
  *      as NaN (a device-side precondition: see below).
  *
  * Strides: non-negative element strides.  The kernels read a query tile
- * (32 rows) and a key tile or decode split (up to 8448 rows) through 32-bit
+ * (32 rows) and a key tile or decode split (up to 8704 rows) through 32-bit
  * buffer windows whose bases are 64-bit: a sequence may span any number of
  * bytes, but that many consecutive rows (row stride x element size) must
  * span less than 4 GiB (GQA_ERR_UNSUPPORTED otherwise).

@@ -318,21 +318,21 @@ def test_negative_strides_rejected():
 
 
 def test_window_spans_below_4gib():
-    """A key tile / decode split (8448 rows) and a query tile (32 rows) are
+    """A key tile / decode split (8704 rows) and a query tile (32 rows) are
     read through 32-bit windows with 64-bit bases: the row stride times that
     many rows must stay below 4 GiB, however long the whole sequence is."""
     # a 262144-token packed KV of 64 heads x 128 f16 spans 4 GiB per tensor
-    # but 8448 rows of it only 138 MB: accepted
+    # but 8704 rows of it only 138 MB: accepted
     a = base_args(PACKED, PACKED, B=1, hq=64, hkv=64, nq=262144, nkv=262144)
     assert st(a) == capi.GQA_OK, capi.last_error()
-    # a row stride of 512 KiB (f16: 262144 elements): 8448 rows reach 4 GiB
+    # a row stride of 512 KiB (f16: 262144 elements): 8704 rows reach 4 GiB
     big = 262144
     a = base_args(PADDED, PACKED, B=1, nkv=100)
     a.k = fake([100, 2, 128], F16, strides=[big, 128, 1])
     a.v = fake([100, 2, 128], F16, strides=[big, 128, 1])
     assert st(a) == capi.GQA_ERR_UNSUPPORTED
     assert "4 GiB" in capi.last_error()
-    # just below: 8448 rows of 256 KiB stride minus a row: 2.2 GB, accepted
+    # just below: 8704 rows of 256 KiB stride minus a row: 2.2 GB, accepted
     a.k = fake([100, 2, 128], F16, strides=[big // 2, 128, 1])
     a.v = fake([100, 2, 128], F16, strides=[big // 2, 128, 1])
     assert st(a) == capi.GQA_OK, capi.last_error()
