@@ -38,16 +38,21 @@ __global__ __launch_bounds__(256) void prefill_plan_kernel(AttnParams p, int32_t
     const int hbase = by * p.heads_per_wg;
     i32x4 r0 = {-1, 0, 0, 0};
     i32x4 r1 = {0, 0, hbase, (hbase / p.group) | (bz << 16)};
-    for (int j = 0; j < 64; ++j) {
-        const int n = s_n[j], incl = s_incl[j];
-        if (n > 0 && bx >= incl - n && bx < incl) {
-            const int b = s_idx[j];
-            const SeqInfo si = s_si[b];
-            r0 = i32x4{b, n - 1 - (bx - (incl - n)), si.q_len, si.kv_len};
-            r1[0] = si.q_start;
-            r1[1] = si.kv_start;
-            break;
-        }
+    // the first sorted entry whose inclusive tile count exceeds bx (the
+    // counts never decrease): its sequence holds position bx
+    int lo = 0, hi = 64;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_incl[mid] > bx) hi = mid;
+        else lo = mid + 1;
+    }
+    if (lo < 64) {
+        const int n = s_n[lo], incl = s_incl[lo];
+        const int b = s_idx[lo];
+        const SeqInfo si = s_si[b];
+        r0 = i32x4{b, n - 1 - (bx - (incl - n)), si.q_len, si.kv_len};
+        r1[0] = si.q_start;
+        r1[1] = si.kv_start;
     }
     i32x4* out = (i32x4*)(rec + (int64_t)L * kWorkRecInts);
     out[0] = r0;
