@@ -488,6 +488,18 @@ def write_trace(cfg: str, trace_dir: str, steps: int = 50) -> dict:
     lines += ["", f"Average of the dominant kernel's last {len(last)} dispatches (the timed steps): "
               f"{avg_ns:.0f} ns.", f"Algorithmic work {work} / {avg_ns / 1e3:.1f} us = {rate:.1f} {unit} "
               f"({rate / peak:.3f} of the {peak:g} {unit} peak)."]
+    # the library's other kernels of each step (tile-map plan, split-KV merge)
+    others = {}
+    for r in trace:
+        n = r["Kernel_Name"]
+        if "gqa" in n and want not in n:
+            others.setdefault(n, []).append(r)
+    for n, rs in sorted(others.items()):
+        rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+        tail = rs[-steps:]
+        ns = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tail) / len(tail)
+        lines.append(f"Also launched in each step: `{n}`, {ns:.0f} ns on average over its last "
+                     f"{len(tail)} dispatches (included in the whole-step rate below).")
     if bench_line:
         lines.append(f"bench.py in the same run (HIP events over the timed steps, whole step): "
                      f"{bench_line['value']} {bench_line['unit']}, {bench_line['ms_per_step']} ms/step.")

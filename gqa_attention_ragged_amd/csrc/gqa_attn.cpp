@@ -69,6 +69,7 @@ struct EnvOverrides {
     bool validate = false;   // GQA_ATTN_VALIDATE=1: device-side length checks before launching
     bool pingpong = false;   // GQA_ATTN_PINGPONG=1: the 8-wave ping-pong kernel where it applies
     bool persist = false;    // GQA_ATTN_PERSIST=1: the persistent prefill kernel where it applies
+    bool records = true;     // GQA_ATTN_RECORDS=0: no tile-map records (every workgroup maps itself)
 };
 
 const EnvOverrides& env_overrides() {
@@ -87,6 +88,7 @@ const EnvOverrides& env_overrides() {
         if (const char* s = std::getenv("GQA_ATTN_VALIDATE")) e.validate = std::atoi(s) != 0;
         if (const char* s = std::getenv("GQA_ATTN_PINGPONG")) e.pingpong = std::atoi(s) != 0;
         if (const char* s = std::getenv("GQA_ATTN_PERSIST")) e.persist = std::atoi(s) != 0;
+        if (const char* s = std::getenv("GQA_ATTN_RECORDS")) e.records = std::atoi(s) != 0;
         return e;
     }();
     return env;
@@ -508,11 +510,14 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // per-workgroup records that a plan kernel writes once per call (the
     // sort and remap that every workgroup would otherwise repeat: about 1.9
     // of a workgroup's 5.3 us outside the key loop); they lead the
-    // workspace.  Worth the extra launch (about 1.6 us) from two rounds of
-    // workgroups on: measured 64 x 256 tokens +7.2%, 64 x 512 +4.2%, 64 x
-    // 128 +2.7%, the ragged causal prefill +0.8%; a 6-workgroup call -18%.
+    // workspace.  Worth the extra launch (about 5 us) from two rounds of
+    // workgroups on, without split-KV: measured 64 x 128 tokens +16%, 64 x
+    // 256 +7%, 64 x 512 +4%, quantized with mask +1.4%, the ragged causal
+    // prefill within noise; a 6-workgroup call -18%, and split-KV grids
+    // (one to three rounds of workgroups plus the merge) -0.6%.
     const int64_t n_wg = (int64_t)plan->grid_x * plan->grid_y * std::max(p.n_splits, 1);
-    if (plan->kernel == K_PREFILL && B <= 64 && n_wg >= kMinRecordWgs) {
+    if (plan->kernel == K_PREFILL && B <= 64 && p.n_splits <= 1 && n_wg >= kMinRecordWgs &&
+        env_overrides().records) {
         plan->rec_bytes =
             ((size_t)n_wg * gqa::kWorkRecInts * sizeof(int32_t) + 255) & ~(size_t)255;
         plan->workspace = plan->rec_bytes + (plan->workspace ? plan->workspace : 256);

@@ -181,17 +181,17 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * selected kernels need none).  Returns a gqa_status_t; *bytes is written
  * on success.
  *
- * What it holds: the decode step's split-KV partials; for prefill with at
- * most 64 sequences and a grid of at least 1024 workgroups, 32 bytes per
- * workgroup (the tile map, computed once per call by a small plan kernel
- * rather than in every workgroup), followed by the split-KV partials when
- * the keys are split.  A prefill call without split-KV also runs when given no (or too
- * little) workspace: each workgroup then builds the map itself (the same
- * map, so the same results; slower).
+ * What it holds: the decode step's split-KV partials, or the prefill
+ * split-KV partials; for prefill without split-KV, with at most 64
+ * sequences and a grid of at least 1024 workgroups, 32 bytes per workgroup
+ * (the tile map, computed once per call by a small plan kernel rather than
+ * in every workgroup).  Such a call also runs when given no (or too little)
+ * workspace: each workgroup then builds the map itself (the same map, so
+ * the same results; slower on short sequences).
  *
  * The kernel plan (and with it the workspace size) is chosen per call from
- * the shapes.  Three environment variables, read once per process (at the
- * first call), override it for measurement: GQA_ATTN_DECODE_SPLIT (keys per
+ * the shapes.  Environment variables, read once per process (at the first
+ * call), override it for measurement: GQA_ATTN_DECODE_SPLIT (keys per
  * decode split, a power of two in 128..8192), GQA_ATTN_PREFILL_SPLITS (key
  * slices of the prefill split-KV path, 1..32), GQA_ATTN_XCD_REMAP=0 (no
  * XCD-aware workgroup order) and GQA_ATTN_PINGPONG=1 (an experimental
@@ -201,7 +201,9 @@ int gqa_attn_validate(const gqa_attn_args_t* args);
  * form of the 4-wave kernel for the same plain case with at most 64
  * sequences: two workgroups per CU claim row tiles in turn and prefetch the
  * next one's first K / V tile and Q rows; faster on short sequences, slower
- * on long ones; needs a workspace of its 512-byte claim counters). */
+ * on long ones; needs a workspace of its 512-byte claim counters) and
+ * GQA_ATTN_RECORDS=0 (no tile-map records: every prefill workgroup builds
+ * the map itself). */
 int gqa_attn_workspace_size(const gqa_attn_args_t* args, size_t* bytes);
 
 /* Compute Y = attention(args) on `stream` (a hipStream_t; NULL = the null
