@@ -181,15 +181,29 @@ struct Decode {
             make_rsrc(kbase + (int64_t)k0 * p.k.sn * KES, rows_bytes(k1 - k0, p.k.sn, D, KES));
         const __amdgpu_buffer_rsrc_t vrs =
             make_rsrc(vbase + (int64_t)k0 * p.v.sn * KES, rows_bytes(k1 - k0, p.v.sn, D, KES));
+        // paged: the page pair of the next tile this wave loads, read from
+        // the table one tile ahead (its latency then overlaps a tile's
+        // compute instead of preceding the tile's loads); a wave loads its
+        // tiles in increasing order, 4 * KT keys apart
+        const int stride = 4 * KT;
+        int pk_next = 0, pv_next = 0;
+        auto fetch_pages = [&](int j) {
+            if constexpr (PAGED) {
+                // the table is read at a clamped index (a tile past the
+                // split's end gets an empty range below)
+                const int pi = min(j, k1 - 1) >> p.page_shift;
+                pk_next = ptk[pi];
+                pv_next = ptk[p.ptab_pages + pi];
+            }
+        };
         auto load = [&](Tile& t, int j0) {
             if constexpr (PAGED) {
                 // a 32-key tile lies inside one page (pages hold a power of
-                // two >= 32 keys); the table is read at a clamped index, and
-                // a tile past the split's end gets an empty range
-                const int pi = min(j0, k1 - 1) >> p.page_shift;
+                // two >= 32 keys)
                 const int within = j0 & ((1 << p.page_shift) - 1);
                 const int valid = min(k1 - j0, KT);
-                const int pk = ptk[pi], pv = ptk[p.ptab_pages + pi];
+                const int pk = pk_next, pv = pv_next;
+                fetch_pages(j0 + stride);
                 const __amdgpu_buffer_rsrc_t kt = make_rsrc(
                     kbase + ((int64_t)pk * p.k.sb + (int64_t)within * p.k.sn) * KES,
                     rows_bytes(valid, p.k.sn, D, KES));
@@ -306,9 +320,9 @@ struct Decode {
         // (16-bit KV) or the next two (fp8 KV) are always issued before the
         // current one is computed (past the split's end they fall outside the
         // buffer range: zeros, no traffic).
-        const int stride = 4 * KT;
         int j0 = k0 + wave * KT;
         if (j0 < k1) {
+            fetch_pages(j0);
             if constexpr (KV8) {
                 // an fp8 tile holds half the bytes of a 16-bit one: the loads
                 // of the next two tiles are in flight while one is computed
