@@ -480,9 +480,14 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
     // 669.  At most 1.25 rounds of workgroups: slices for about 3 rounds.
     const bool can_split = a->norm == GQA_NORM_SOFTMAX && a->qdq == GQA_QDQ_OFF &&
                            qdt != GQA_DT_FP8_E4M3 && kv_tiles >= 8;
+    // With padded Q the grid is exact (no ragged slack): when it fills most
+    // of one round of workgroups, slices add partials and the merge but no
+    // balance (tree decoding, 512 workgroups: one slice 731 TFLOP/s, three
+    // 675); a packed grid is an upper bound and keeps the rule above.
+    const bool full_round = qf == GQA_FORM_PADDED_BHND && wgs >= slots * 3 / 4 && wgs <= slots;
     if (can_split) {
         int64_t S = 1;
-        if (wgs < slots * 5 / 4) {
+        if (wgs < slots * 5 / 4 && !full_round) {
             S = (3 * slots + wgs - 1) / wgs;
             S = std::min<int64_t>(S, std::min<int64_t>(kv_tiles / 4, 32));  // <= 64: combine kernel
         }
