@@ -427,3 +427,21 @@ def test_check_lengths_needs_host_copies():
     a = _lens_args()
     assert _chk(a, None, [60, 0, 80]) == capi.GQA_ERR_INVALID_ARG
     assert "host copy" in capi.last_error()
+
+
+def test_split_kv_planning():
+    """Key slices for prefill: a padded-Q grid that fills 3/4 to one round of
+    the 512 workgroup slots takes none (tree decoding shape: 32 sequences x 64
+    drafts x 8 head groups = 512 workgroups); half a round, or a packed grid
+    (an upper bound), over long keys takes slices (the workspace holds their
+    fp32 partials)."""
+    full = base_args(PADDED, PADDED, B=32, hq=32, hkv=8, nq=64, nkv=8192)
+    assert capi.gqa_attn_workspace_size(full) == 0
+    half = base_args(PADDED, PADDED, B=16, hq=32, hkv=8, nq=64, nkv=8192)
+    assert capi.gqa_attn_workspace_size(half) > 16 * 64 * 32 * 2 * 128 * 4
+    # 24 sequences: padded, 384 workgroups (3/4 of a round): none; packed, an
+    # upper bound of 576 workgroups: slices
+    assert capi.gqa_attn_workspace_size(
+        base_args(PADDED, PADDED, B=24, hq=32, hkv=8, nq=64, nkv=8192)) == 0
+    packed = base_args(PACKED, PADDED, B=24, hq=32, hkv=8, nq=64, nkv=8192)
+    assert capi.gqa_attn_workspace_size(packed) > 24 * 64 * 32 * 2 * 128 * 4
