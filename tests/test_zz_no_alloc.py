@@ -81,6 +81,29 @@ def test_noalloc_prefill_split_two_calls_second_smaller():
     parity.compare(small, b)
 
 
+def test_noalloc_prefill_records_two_calls_second_smaller():
+    # at least 1024 workgroups and no key slices: the static buffer holds the
+    # tile-map records, and the second, smaller call rewrites fewer of them
+    rng = np.random.default_rng(8300)
+    ql = rng.integers(64, 400, size=64)
+    kl = ql + rng.integers(0, 40, size=64)
+    big = synth.generate(seed=8300, q_lens=ql, kv_lens=kl, num_heads=32, kv_num_heads=8,
+                         head_dim=128, query_form="packed_nhd", kv_form="packed_nhd",
+                         q_slack=2, kv_slack=2, dtype=torch.bfloat16, causal_kind="lower_right",
+                         device=DEV, name="noalloc-records-big")
+    a, b = _both(big)
+    _check_pair(big, a, b)
+    ql2 = rng.integers(100, 300, size=40)
+    small = synth.generate(seed=8301, q_lens=ql2, kv_lens=ql2 + 7, num_heads=32,
+                           kv_num_heads=8, head_dim=128, query_form="packed_nhd",
+                           kv_form="padded_bhnd", n_kv=int(ql2.max()) + 9, q_slack=2,
+                           dtype=torch.float16, causal_kind="none", device=DEV,
+                           name="noalloc-records-small")
+    a, b = _both(small)
+    _check_pair(small, a, b)
+    parity.compare(small, b)
+
+
 def test_noalloc_rejects_beyond_static_buffer():
     # 512 sequences x 32 heads x 32 key splits of partials: more than 128 MiB
     # of workspace.  K / V are stride-0 views of one row (the call is
