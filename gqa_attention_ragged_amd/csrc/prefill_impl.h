@@ -152,15 +152,18 @@ constexpr int kWaitLgkmcnt0 = 0xC07F;
 // Mask variants of the general kernel: none; read per lane from global memory
 // (any kind and layout); staged through LDS as 16-bit additive values -- f16
 // (an f16 mask, or a bool mask converted to 0 / -inf while staging) or bf16;
-// no mask but tree decoding.  The tree rule is compiled only into the
-// generic and tree variants (a tree with a mask takes the generic one).
-enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3, MK_TREE = 4 };
+// no mask but tree decoding; staged bool masks in the fp8 kernels, whose
+// mask type is then known at compile time (fewer registers: three
+// workgroups per CU).  The tree rule is compiled only into the generic and
+// tree variants (a tree with a mask takes the generic one).
+enum MaskVariant { MK_NONE = 0, MK_GENERIC = 1, MK_LDS16 = 2, MK_LDS_BF16 = 3, MK_TREE = 4,
+                   MK_LDS_BOOL = 5 };
 
 template <typename TI, int D, int MK, bool PAGED = false, bool KV8 = false>
 struct Prefill {
     static constexpr bool HAS_MASK = MK != MK_NONE && MK != MK_TREE;
     static constexpr bool TREE = MK == MK_GENERIC || MK == MK_TREE;  // tree rule compiled in
-    static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16;
+    static constexpr bool STAGED = MK == MK_LDS16 || MK == MK_LDS_BF16 || MK == MK_LDS_BOOL;
     typedef Cfg<TI, D> C;
     // MFMA element type: the input type for 16-bit inputs; E4M3FN codes for fp8.
     typedef typename std::conditional<C::FP8, f16, TI>::type T16;
@@ -173,15 +176,14 @@ struct Prefill {
     // score; 16-bit kernels (whose LDS holds only 16-bit values for two
     // workgroups per CU) stage the 16-bit values and add them per score.
     static constexpr bool MACC = STAGED && C::FP8;
+    static_assert(MK != MK_LDS_BOOL || C::FP8, "compile-time bool staging: fp8 kernels");
     static constexpr int MROW = MACC ? C::BN * 4 + 16 : C::MROW;
     static constexpr int MBYTES = 32 * MROW;
     // Bytes per pipeline stage: K tile, V tile and (mask kernels) a mask tile.
     static constexpr int SSTAGE = C::STAGE + (HAS_MASK ? MBYTES : 0);
     // When a tile's copy instructions do not divide evenly over the 4 waves,
-    // the waves without a last instruction still issue one (every lane out
-    // of range: zeros, no memory access) into a spare 1 KiB after the stage,
-    // so that the copy has no wave-dependent branches.
-    static constexpr int SPARE = (C::NKD % 4 || C::NVD % 4) ? 1024 : 0;
+    // the waves without a last instruction skip it (a wave-uniform branch:
+    // every wait for the copies is a wait for all of the wave's loads).
     // fp8 KV cache with 16-bit Q (KV8): K / V tiles are copied as E4M3FN codes
     // in unpadded rows of D bytes into small stages (an even number of 1 KiB
     // copies per wave: no spare) and converted once per tile, by the whole
@@ -236,6 +238,12 @@ struct Prefill {
         bool tree_over;       // row beyond the drafts this build resolves: its output is NaN
     };
 
+    // Staged bool mask?  Known at compile time in the fp8 kernels (bool masks
+    // take MK_LDS_BOOL there), a flag of the call in the 16-bit ones.
+    __device__ __forceinline__ static bool mask_is_bool(const Ctx& c) {
+        return MACC ? MK == MK_LDS_BOOL : c.mbool;
+    }
+
     // Drafts per sequence whose ancestor chains the tree variants resolve
     // (two per lane).
     static constexpr int kMaxDrafts = 128;
@@ -284,7 +292,7 @@ struct Prefill {
         const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
         const int64_t off = (int64_t)tile * (C::BN * es);
         const __amdgpu_buffer_rsrc_t mr = make_rsrc(c.mtile + off, clamp_range(c.mvalid - off));
-        if (MACC && c.mbool) {
+        if (MACC && mask_is_bool(c)) {
             u32x2 v;  // fp8 kernels stage bool masks in 8-byte chunks
             buf_load(mr, c.moff, v);
             rm[0] = v[0];
@@ -301,7 +309,7 @@ struct Prefill {
         if (c.mrow_l < 0) return;
         char* row = stage + C::STAGE + c.mrow_l * MROW;
         if constexpr (MACC) {
-            if (c.mbool) {
+            if (mask_is_bool(c)) {
                 // 8 keys: byte b -> bias (b - 1) & 0xFF800000, i.e. -inf for
                 // a zero byte and +0 for any other (b - 1 < 2^23)
 #pragma unroll
@@ -410,15 +418,15 @@ struct Prefill {
 #pragma unroll
         for (int k = 0; k < C::KMAX; ++k) {
             const int j = wave + 4 * k;
-            const int dst = 4 * (k + 1) <= C::NKD || j < C::NKD ? j * 1024 : SSTAGE;
-            buf_load_lds16_async<PAGED>(kr, stage + dst, c.koff[k]);
+            if (4 * (k + 1) <= C::NKD || j < C::NKD)
+                buf_load_lds16_async<PAGED>(kr, stage + j * 1024, c.koff[k]);
         }
         if (!with_v) return;
 #pragma unroll
         for (int k = 0; k < C::VMAX; ++k) {
             const int j = wave + 4 * k;
-            const int dst = 4 * (k + 1) <= C::NVD || j < C::NVD ? C::KBYTES + j * 1024 : SSTAGE;
-            buf_load_lds16_async<PAGED>(vr, stage + dst, c.voff[k]);
+            if (4 * (k + 1) <= C::NVD || j < C::NVD)
+                buf_load_lds16_async<PAGED>(vr, stage + C::KBYTES + j * 1024, c.voff[k]);
         }
     }
 
@@ -468,25 +476,50 @@ struct Prefill {
         const char* row0 = sK + lr * C::KROW;
         const char* row1 = sK + (32 + lr) * C::KROW;
         if constexpr (C::FP8) {
-            // every K operand of the tile (one or two 64-byte k-steps per
-            // key block) read before the first MFMA, which then waits for
-            // its own reads only (sched_barrier keeps the order)
-            i32x8 a[C::QSTEPS][2];
+            auto kop = [&](int ks, int kb) {
+                const char* row = kb ? row1 : row0;
+                const u32x4 lo = *(const u32x4*)(row + ks * 64 + lg * 32);
+                const u32x4 hi = *(const u32x4*)(row + ks * 64 + lg * 32 + 16);
+                i32x8 a;
+                a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                return a;
+            };
+            if constexpr (MACC) {
+                // Staged biases occupy the accumulators before the MFMAs:
+                // the two K operands of one 64-byte k-step at a time, the
+                // next k-step's reads issued behind the current two MFMAs
+                // (128 cycles of matrix work cover their latency) into the
+                // same registers, 16 VGPRs fewer than reading the whole tile
+                // first (sched_barrier keeps the order).
+                i32x8 a0 = kop(0, 0), a1 = kop(0, 1);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < C::QSTEPS; ++ks)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const char* row = kb ? row1 : row0;
-                    const u32x4 lo = *(const u32x4*)(row + ks * 64 + lg * 32);
-                    const u32x4 hi = *(const u32x4*)(row + ks * 64 + lg * 32 + 16);
-                    a[ks][kb][0] = lo[0]; a[ks][kb][1] = lo[1]; a[ks][kb][2] = lo[2]; a[ks][kb][3] = lo[3];
-                    a[ks][kb][4] = hi[0]; a[ks][kb][5] = hi[1]; a[ks][kb][6] = hi[2]; a[ks][kb][7] = hi[3];
+                for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                    s[0] = mfma32_fp8(a0, qreg[ks], s[0]);
+                    s[1] = mfma32_fp8(a1, qreg[ks], s[1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (ks + 1 < C::QSTEPS) {
+                        a0 = kop(ks + 1, 0);
+                        a1 = kop(ks + 1, 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
-            __builtin_amdgcn_sched_barrier(0);
+            } else {
+                // every K operand of the tile read before the first MFMA,
+                // which then waits for its own reads only
+                i32x8 a[C::QSTEPS][2];
 #pragma unroll
-            for (int ks = 0; ks < C::QSTEPS; ++ks) {
-                s[0] = mfma32_fp8(a[ks][0], qreg[ks], s[0]);
-                s[1] = mfma32_fp8(a[ks][1], qreg[ks], s[1]);
+                for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                    a[ks][0] = kop(ks, 0);
+                    a[ks][1] = kop(ks, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < C::QSTEPS; ++ks) {
+                    s[0] = mfma32_fp8(a[ks][0], qreg[ks], s[0]);
+                    s[1] = mfma32_fp8(a[ks][1], qreg[ks], s[1]);
+                }
             }
         } else {
             // Explicit software pipeline (the source order is the
@@ -1128,14 +1161,14 @@ struct Prefill {
         c.moff = 0;
         c.mrow_l = -1;
         c.mchunk = 0;
-        c.mbool = p.mask_kind == MASK_BOOL;
+        c.mbool = p.mask_kind == MASK_BOOL;  // MK_LDS_BOOL: the host launched it for a bool mask
         if constexpr (STAGED) {
             // 32 rows x BN keys; 16-bit: 8 chunks of 16 B per row (all 256
             // threads); bool: 4 chunks of 16 B per row (threads 0..127),
             // or in the fp8 kernels, whose staging expands each byte to four,
             // 8 chunks of 8 B (all 256 threads)
             const int es = p.mask_kind == MASK_BOOL ? 1 : 2;
-            const int chunk = MACC && c.mbool ? 8 : 16;
+            const int chunk = MACC && mask_is_bool(c) ? 8 : 16;
             const int cpr = C::BN * es / chunk;
             if (tid < 32 * cpr) {
                 c.mrow_l = tid / cpr;
@@ -1330,19 +1363,23 @@ struct Prefill {
 // normalization kernels at D = 128, whose split BMM2 needs more registers:
 // one workgroup per CU, so that no kernel uses scratch memory (scratch loads
 // would share vmcnt with the direct-to-LDS tile copies that the key loop
-// waits on by hand).
-template <typename TI, int D, int MODE>
+// waits on by hand).  The fp8 Q/DQ kernels with a staged bool mask fit
+// three (<= 168 VGPRs, 3 x 52 KB of LDS), as the mask-free fp8 kernels do by
+// themselves; the online fp8 one would spill there and keeps two.
+template <typename TI, int D, int MODE, int MK>
 constexpr int kPrefillWgsPerCu =
-    MODE == MODE_NONE && D == 128 && !std::is_same<TI, fp8>::value ? 1 : 2;
+    MODE == MODE_NONE && D == 128 && !std::is_same<TI, fp8>::value ? 1
+    : MK == MK_LDS_BOOL && (MODE == MODE_SOFTMAX_QDQ || MODE == MODE_SOFTMAX_QDQ_NS) ? 3
+                                                                                     : 2;
 
 template <typename TI, int D, int MODE, int MK, bool PAGED = false>
-__global__ __launch_bounds__(256, (kPrefillWgsPerCu<TI, D, MODE>)) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, (kPrefillWgsPerCu<TI, D, MODE, MK>)) void prefill_kernel(AttnParams p) {
     // two separate stage arrays: the compiler then knows that the copy into
     // one stage never aliases the reads of the other, and does not wait for
     // the copy before computing on the current stage
     typedef Prefill<TI, D, MK, PAGED> P;
-    __shared__ __attribute__((aligned(16))) char st0[P::SSTAGE + P::SPARE];
-    __shared__ __attribute__((aligned(16))) char st1[P::SSTAGE + P::SPARE];
+    __shared__ __attribute__((aligned(16))) char st0[P::SSTAGE];
+    __shared__ __attribute__((aligned(16))) char st1[P::SSTAGE];
     P::template run<MODE>(p, st0, st1);
 }
 
@@ -1453,6 +1490,9 @@ static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t st
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_GENERIC>), grid, dim3(256), 0, stream, p);
     else if (p.mask_kind == MASK_BF16)
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS_BF16>), grid, dim3(256), 0, stream, p);
+    else if (std::is_same<TI, fp8>::value && p.mask_kind == MASK_BOOL)
+        hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, (std::is_same<TI, fp8>::value ? MK_LDS_BOOL : MK_LDS16)>),
+                           grid, dim3(256), 0, stream, p);
     else
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS16>), grid, dim3(256), 0, stream, p);
 }

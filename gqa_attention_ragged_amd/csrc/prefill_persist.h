@@ -557,8 +557,8 @@ struct Persist {
 template <typename TI, int D>
 __global__ __launch_bounds__(256, 2) void prefill_persist_kernel(AttnParams p) {
     typedef Persist<TI, D> K;
-    __shared__ __attribute__((aligned(16))) char st0[K::P::SSTAGE + K::P::SPARE];
-    __shared__ __attribute__((aligned(16))) char st1[K::P::SSTAGE + K::P::SPARE];
+    __shared__ __attribute__((aligned(16))) char st0[K::P::SSTAGE];
+    __shared__ __attribute__((aligned(16))) char st1[K::P::SSTAGE];
     K::run(p, st0, st1);
 }
 

@@ -156,6 +156,25 @@ def test_fp8_staged_masks(mask, norm, qdq):
     parity.compare(c, parity.run_gpu(c))
 
 
+@pytest.mark.parametrize("D,qscale", [(64, 1 / 448.0), (64, 1 / 2000.0), (128, 1 / 2000.0)])
+def test_fp8_bool_mask_kernels(D, qscale):
+    # fp8 kernels with a staged bool mask (bool known at compile time, three
+    # workgroups per CU) in both Q/DQ variants: a small qscale keeps the
+    # quantizer's clamp, 1/448 takes the clamp-free one; ragged rows and
+    # keys, a mask with rows of no allowed key besides the forced diagonal.
+    seed = 290 + D + int(1 / qscale) % 13
+    ql = np.array([45, 1, 96, 0, 33, 64])
+    kl = np.array([301, 40, 333, 19, 77, 64])
+    c = synth.generate(seed=seed, q_lens=ql, kv_lens=np.maximum(kl, ql), num_heads=8,
+                       kv_num_heads=2, head_dim=D, query_form="packed_nhd",
+                       kv_form="padded_bhnd", n_kv=352, q_slack=2, kv_slack=0,
+                       dtype=torch.float8_e4m3fn, dist="round_normal", mask_kind="bool",
+                       mask_p=0.35, mask_diag_true=True, causal_kind="lower_right",
+                       norm="softmax", qdq="fp8", qscale=float(np.float32(qscale)),
+                       device=DEV, name=f"fp8-bool-D{D}-{int(1 / qscale)}")
+    parity.compare(c, parity.run_gpu(c), amb_rel=1e-4)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("heads", [(4, 4), (8, 4), (8, 2), (8, 1), (12, 4), (6, 2)])
 def test_head_groups_and_head_size(D, heads):
