@@ -132,19 +132,28 @@ def make_step(case):
 # requested step count, makes the timed steps steady state.
 MIN_WARMUP_MS = 400.0
 _warmup_log: dict = {}
+# Average duration of the main attention kernel over the timed steps (ms),
+# from the library's own event pairs around that kernel (gqa_attn_timer_*).
+_kernel_ms: dict = {}
 
 
-def time_steps(step, steps: int, warmup: int, tag: str = "") -> float:
+def time_steps(step, steps: int, warmup: int, tag: str = "", kernel_timer: bool = False,
+               min_warmup_ms: float = MIN_WARMUP_MS) -> float:
     """Average ms per step over `steps` timed launches (HIP events on the
     stream the kernels run on), after `warmup` steps and as many more as it
-    takes to reach MIN_WARMUP_MS of warm-up (recorded in _warmup_log)."""
+    takes to reach min_warmup_ms of warm-up (recorded in _warmup_log).  With
+    kernel_timer, the library also times its main kernel in each timed step
+    (an event pair on the same stream around that kernel alone): the average
+    goes to _kernel_ms[tag].  The event records add a few microseconds per
+    step, so whole-step rates come from runs without them."""
     import torch
+    from gqa_attention_ragged_amd import capi
     t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     extra = 0
-    while (time.perf_counter() - t0) * 1e3 < MIN_WARMUP_MS:
+    while (time.perf_counter() - t0) * 1e3 < min_warmup_ms:
         for _ in range(10):
             step()
         extra += 10
@@ -153,11 +162,19 @@ def time_steps(step, steps: int, warmup: int, tag: str = "") -> float:
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    if kernel_timer and capi.timer_start(steps) != capi.GQA_OK:
+        raise RuntimeError(f"gqa_attn_timer_start: {capi.last_error()}")
     start.record(stream)
     for _ in range(steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
+    if kernel_timer:
+        st, kms, n = capi.timer_stop()
+        if st != capi.GQA_OK or n != steps:
+            raise RuntimeError(f"gqa_attn_timer_stop: status {st}, {n} of {steps} steps timed: "
+                               f"{capi.last_error()}")
+        _kernel_ms[tag] = kms / n
     return start.elapsed_time(end) / steps
 
 
@@ -196,20 +213,28 @@ def measure(cfg: str, steps: int, warmup: int) -> dict:
     case = synth.make_config(cfg, device="cuda")
     torch.cuda.synchronize()
     w = work_of(case)
-    ms = time_steps(make_step(case), steps, warmup, cfg)
+    step = make_step(case)
+    ms = time_steps(step, steps, warmup, cfg)
+    # the main kernel's own duration: the same number of steps again, right
+    # after the timed ones (clocks warm), with the library's event pair
+    # around that kernel in each step
+    time_steps(step, steps, 0, cfg + ":kernel", kernel_timer=True, min_warmup_ms=0.0)
+    kms = _kernel_ms[cfg + ":kernel"]
     dt = dtype_name(case)
     r = {"workload": cfg, "description": synth.DESCRIPTIONS[cfg], "ms_per_step": round(ms, 4),
-         "dtype": dt}
+         "kernel_ms": round(kms, 4), "dtype": dt}
     if cfg == "1":
         r["latency_us"] = round(ms * 1e3, 2)  # one call, latency-bound
     if w["kind"] == "decode":
         gbs = w["bytes"] / (ms * 1e-3) / 1e9
         r.update(metric="KV GB/s", value=round(gbs, 1), unit="GB/s", bytes=w["bytes"],
-                 roofline_frac=round(gbs / HBM_PEAK, 4), bound="hbm", peak=HBM_PEAK)
+                 roofline_frac=round(gbs / HBM_PEAK, 4), bound="hbm", peak=HBM_PEAK,
+                 kernel_value=round(w["bytes"] / (kms * 1e-3) / 1e9, 1))
     else:
         tf = w["flop"] / (ms * 1e-3) / 1e12
         r.update(metric="attention TFLOP/s", value=round(tf, 1), unit="TFLOP/s", flop=w["flop"],
-                 roofline_frac=round(tf / PEAK[dt], 4), bound="mfma", peak=PEAK[dt])
+                 roofline_frac=round(tf / PEAK[dt], 4), bound="mfma", peak=PEAK[dt],
+                 kernel_value=round(w["flop"] / (kms * 1e-3) / 1e12, 1))
     r["_case"] = case
     return r
 
@@ -503,6 +528,13 @@ def write_trace(cfg: str, trace_dir: str, steps: int = 50) -> dict:
     if bench_line:
         lines.append(f"bench.py in the same run (HIP events over the timed steps, whole step): "
                      f"{bench_line['value']} {bench_line['unit']}, {bench_line['ms_per_step']} ms/step.")
+        roof = bench_line.get("roofline") or {}
+        if roof.get("kernel_ms") is not None:
+            kns = roof["kernel_ms"] * 1e6
+            lines.append(f"bench.py's own timing of this kernel (the library's event pair around it, "
+                         f"in a second pass of the timed steps): {kns:.0f} ns on average, {roof['achieved']} "
+                         f"{roof['unit']} (roofline.achieved); the trace's average above: "
+                         f"{avg_ns:.0f} ns ({(kns / avg_ns - 1) * 100:+.1f}%).")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     return {"workload": cfg, "kernel": kernel, "avg_ns": avg_ns, "rate": rate, "unit": unit, "path": path}
@@ -640,11 +672,14 @@ def main() -> int:
     kind = "decode" if main_r["bound"] == "hbm" else "prefill"
     per_launch = main_r["bytes"] if kind == "decode" else main_r["flop"]
     traffic = traffic_for(a.workload, kind)
-    ach = main_r["value"]
+    # the main kernel's own rate: algorithmic work per launch over its
+    # average duration (the library's event pairs, in a second pass of the
+    # timed steps)
+    ach = main_r["kernel_value"]
     roof = {"bound": main_r["bound"], "achieved": ach, "peak": main_r["peak"],
             "unit": main_r["unit"], "frac": round(ach / main_r["peak"], 4), "traffic": traffic,
             "kernel": kernel_name(case, kind),
-            "per_launch": per_launch}
+            "per_launch": per_launch, "kernel_ms": main_r["kernel_ms"]}
     secondary = {}
     if not a.no_secondary:
         for cfg in WORKLOADS:

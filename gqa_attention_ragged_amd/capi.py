@@ -119,6 +119,11 @@ def load() -> ctypes.CDLL:
         I32 = ctypes.POINTER(ctypes.c_int32)
         lib.gqa_attn_check_lengths.argtypes = [P, I32, I32, I32]
         lib.gqa_attn_check_lengths.restype = ctypes.c_int
+        lib.gqa_attn_timer_start.argtypes = [ctypes.c_int]
+        lib.gqa_attn_timer_start.restype = ctypes.c_int
+        lib.gqa_attn_timer_stop.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_int)]
+        lib.gqa_attn_timer_stop.restype = ctypes.c_int
         K = ctypes.POINTER(GqaKvUpdateArgs)
         lib.gqa_kv_cache_update_validate.argtypes = [K]
         lib.gqa_kv_cache_update_validate.restype = ctypes.c_int
@@ -134,6 +139,18 @@ def status_str(status: int) -> str:
 
 def last_error() -> str:
     return load().gqa_attn_last_error().decode()
+
+
+def timer_start(max_launches: int) -> int:
+    """Open the library's main-kernel timing window (gqa_attn_timer_start)."""
+    return load().gqa_attn_timer_start(int(max_launches))
+
+
+def timer_stop():
+    """Close the window: (status, summed main-kernel ms, timed calls)."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int(0)
+    st = load().gqa_attn_timer_stop(ctypes.byref(ms), ctypes.byref(n))
+    return st, ms.value, n.value
 
 
 def tensor_view(t: Optional[torch.Tensor]) -> GqaTensor:

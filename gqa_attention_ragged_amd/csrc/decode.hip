@@ -30,6 +30,7 @@
 //     and writes the output row.
 #include "device_common.h"
 #include "launch.h"
+#include "main_timer.h"
 
 #include <type_traits>
 
@@ -429,12 +430,14 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(AttnParams p) {
 
 template <typename TQ, typename TKV, int D>
 static hipError_t launch_t(const AttnParams& p, hipStream_t stream) {
+    main_kernel_begin(stream);
     if (p.kv_paged)
         hipLaunchKernelGGL((decode_split_kernel<TQ, TKV, D, true>), dim3(p.hkv, p.batch, p.n_splits),
                            dim3(256), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_split_kernel<TQ, TKV, D, false>), dim3(p.hkv, p.batch, p.n_splits),
                            dim3(256), 0, stream, p);
+    main_kernel_end(stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((decode_combine_kernel<TQ, D>), dim3(p.hq, p.batch), dim3(D), 0, stream, p);

@@ -15,14 +15,36 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "launch.h"
 #include "lengths.h"
+#include "main_timer.h"
 
 namespace {
 
 thread_local char g_err[256];
 thread_local int g_hip_err = 0;
+
+// Main-kernel timing window (gqa_attn_timer_start / _stop): event pairs
+// recorded around the main kernel of each call while the window is open.
+struct MainTimer {
+    std::atomic<bool> on{false};
+    std::mutex mu;
+    std::vector<hipEvent_t> ev;  // pair i: ev[2i] before, ev[2i + 1] after
+    int used = 0;                // pairs recorded
+    bool pending = false;        // ev[2 * used] recorded, its partner not yet
+    hipError_t err = hipSuccess;
+};
+MainTimer& main_timer() {
+    static MainTimer t;
+    return t;
+}
+void destroy_events(MainTimer& t) {
+    for (hipEvent_t e : t.ev) (void)hipEventDestroy(e);
+    t.ev.clear();
+}
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -539,6 +561,28 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
 
 }  // namespace
 
+namespace gqa {
+void main_kernel_begin(hipStream_t stream) {
+    MainTimer& t = main_timer();
+    if (!t.on.load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.on.load(std::memory_order_relaxed) || 2 * t.used >= (int)t.ev.size()) return;
+    const hipError_t e = hipEventRecord(t.ev[2 * t.used], stream);
+    if (e != hipSuccess) t.err = e;
+    t.pending = e == hipSuccess;
+}
+void main_kernel_end(hipStream_t stream) {
+    MainTimer& t = main_timer();
+    if (!t.on.load(std::memory_order_acquire)) return;
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.pending) return;
+    const hipError_t e = hipEventRecord(t.ev[2 * t.used + 1], stream);
+    if (e != hipSuccess) t.err = e;
+    else ++t.used;
+    t.pending = false;
+}
+}  // namespace gqa
+
 extern "C" {
 
 int gqa_attn_validate(const gqa_attn_args_t* args) {
@@ -801,10 +845,59 @@ int gqa_kv_cache_update(const gqa_kv_update_args_t* args, void* stream) {
     return GQA_OK;
 }
 
+int gqa_attn_timer_start(int max_launches) {
+    if (max_launches <= 0) return fail(GQA_ERR_INVALID_ARG, "max_launches must be > 0");
+    MainTimer& t = main_timer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.on.load()) return fail(GQA_ERR_INVALID_ARG, "a timing window is already open");
+    t.ev.assign(2 * (size_t)max_launches, nullptr);
+    for (size_t i = 0; i < t.ev.size(); ++i) {
+        const hipError_t e = hipEventCreate(&t.ev[i]);
+        if (e != hipSuccess) {
+            t.ev.resize(i);
+            destroy_events(t);
+            g_hip_err = (int)e;
+            return fail(GQA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+    }
+    t.used = 0;
+    t.pending = false;
+    t.err = hipSuccess;
+    t.on.store(true, std::memory_order_release);
+    return GQA_OK;
+}
+
+int gqa_attn_timer_stop(double* total_ms, int* launches) {
+    if (!total_ms || !launches) return fail(GQA_ERR_INVALID_ARG, "null output pointer");
+    MainTimer& t = main_timer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.on.load()) return fail(GQA_ERR_INVALID_ARG, "no timing window is open");
+    t.on.store(false, std::memory_order_release);
+    hipError_t e = t.err;
+    double sum = 0.0;
+    for (int i = 0; i < t.used && e == hipSuccess; ++i) {
+        e = hipEventSynchronize(t.ev[2 * i + 1]);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
+        sum += ms;
+    }
+    const int n = t.used;
+    destroy_events(t);
+    t.used = 0;
+    t.pending = false;
+    if (e != hipSuccess) {
+        g_hip_err = (int)e;
+        return fail(GQA_ERR_HIP, "main-kernel timing: %s", hipGetErrorString(e));
+    }
+    *total_ms = sum;
+    *launches = n;
+    return GQA_OK;
+}
+
 const char* gqa_attn_last_error(void) { return g_err; }
 
 int gqa_attn_last_hip_error(void) { return g_hip_err; }
 
-int gqa_attn_abi_version(void) { return 5; }
+int gqa_attn_abi_version(void) { return 6; }
 
 }  // extern "C"

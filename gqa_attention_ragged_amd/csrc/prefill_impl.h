@@ -36,6 +36,7 @@
 #pragma once
 #include "device_common.h"
 #include "launch.h"
+#include "main_timer.h"
 #include "tile_common.h"
 
 #include <type_traits>
@@ -1464,7 +1465,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(AttnParams p) {
 }
 
 template <typename TI, int D, int MODE>
-static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+static void launch_m_kernel(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
     if constexpr (MODE == MODE_SOFTMAX && !std::is_same<TI, fp8>::value) {
         // paged KV: online softmax only (host-checked); masks are read per
@@ -1496,12 +1497,19 @@ static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t st
     else
         hipLaunchKernelGGL((prefill_kernel<TI, D, MODE, MK_LDS16>), grid, dim3(256), 0, stream, p);
 }
+template <typename TI, int D, int MODE>
+static void launch_m(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
+    main_kernel_begin(stream);
+    launch_m_kernel<TI, D, MODE>(p, grid_x, grid_y, stream);
+    main_kernel_end(stream);
+}
 
 // fp8 KV cache with 16-bit Q (online softmax; masks read per lane), then the
 // split-KV merge when the keys are split.
 template <typename TI, int D>
 static hipError_t launch_kv8_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
+    main_kernel_begin(stream);
     if (p.kv_paged) {
         if (p.mask_kind != MASK_NONE)
             hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_GENERIC, true>), grid, dim3(256), 0, stream, p);
@@ -1517,6 +1525,7 @@ static hipError_t launch_kv8_t(const AttnParams& p, int grid_x, int grid_y, hipS
         else
             hipLaunchKernelGGL((prefill_kv8_kernel<TI, D, MK_NONE, false>), grid, dim3(256), 0, stream, p);
     }
+    main_kernel_end(stream);
     if (p.n_splits > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

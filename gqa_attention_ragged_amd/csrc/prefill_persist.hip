@@ -12,7 +12,9 @@ static hipError_t launch_persist_t(const AttnParams& p, int workgroups, hipStrea
                        kSchedInts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    main_kernel_begin(stream);
     hipLaunchKernelGGL((prefill_persist_kernel<TI, D>), dim3(workgroups), dim3(256), 0, stream, p);
+    main_kernel_end(stream);
     if (p.n_splits > 1) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -7,7 +7,9 @@ namespace gqa {
 template <typename TI, int D>
 static hipError_t launch_pp_t(const AttnParams& p, int grid_x, int grid_y, hipStream_t stream) {
     const dim3 grid(grid_x, grid_y, p.n_splits > 1 ? p.n_splits : 1);
+    main_kernel_begin(stream);
     hipLaunchKernelGGL((prefill_pp_kernel<TI, D>), grid, dim3(512), 0, stream, p);
+    main_kernel_end(stream);
     if (p.n_splits > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -248,6 +248,25 @@ int gqa_attn_forward_noalloc(const gqa_attn_args_t* args, void* stream);
 int gqa_attn_check_lengths(const gqa_attn_args_t* args, const int32_t* query_lengths_host,
                            const int32_t* kv_lengths_host, const int32_t* kv_page_table_host);
 
+/* Timing of the main kernel, for measurement.  gqa_attn_timer_start opens a
+ * window of at most max_launches (> 0) timed calls on the current device:
+ * it creates 2 x max_launches HIP events, and every later gqa_attn_forward
+ * or gqa_attn_forward_noalloc call records one pair of them on its stream,
+ * right before and right after its main kernel (the prefill attention
+ * kernel, or the decode split kernel; the tile-map plan kernel, the split-KV
+ * merge, the decode combine and the length check fall outside), until the
+ * pairs run out: later calls are not timed.  gqa_attn_timer_stop waits for
+ * the recorded events, writes the summed main-kernel time in milliseconds
+ * to *total_ms and the number of timed calls to *launches, destroys the
+ * events and closes the window.  Errors: GQA_ERR_INVALID_ARG (max_launches
+ * <= 0, a window already open or none open, a null output pointer),
+ * GQA_ERR_HIP (creating, recording or timing the events failed; the window
+ * is closed).  One window per process, shared by all threads (its records
+ * are serialized by the library).  Not for calls under graph capture (the
+ * event records would be captured with them). */
+int gqa_attn_timer_start(int max_launches);
+int gqa_attn_timer_stop(double* total_ms, int* launches);
+
 /* Human-readable text of a status code (static storage). */
 const char* gqa_attn_status_str(int status);
 
@@ -260,7 +279,7 @@ int gqa_attn_last_hip_error(void);
 
 /* Library ABI version (bumped on any change of these declarations or of
  * those in gqa_kv_cache.h; 2 adds the KV-cache update, 3 tree_parents, 4 paged
- * KV, 5 gqa_attn_check_lengths and 128-draft trees). */
+ * KV, 5 gqa_attn_check_lengths and 128-draft trees, 6 the main-kernel timer). */
 int gqa_attn_abi_version(void);
 
 #ifdef __cplusplus

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     assert "gqa_kv_cache_update" in names and "gqa_kv_cache_update_validate" in names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.gqa_attn_abi_version() == 5
+    assert lib.gqa_attn_abi_version() == 6
     assert "gqa_attn_check_lengths" in names
 
 
@@ -445,3 +445,14 @@ def test_split_kv_planning():
         base_args(PADDED, PADDED, B=24, hq=32, hkv=8, nq=64, nkv=8192)) == 0
     packed = base_args(PACKED, PADDED, B=24, hq=32, hkv=8, nq=64, nkv=8192)
     assert capi.gqa_attn_workspace_size(packed) > 24 * 64 * 32 * 2 * 128 * 4
+
+
+def test_timer_argument_errors():
+    # the main-kernel timer's host-side checks (no HIP call is made): a
+    # window needs a positive size, a stop needs an open window and outputs
+    lib = capi.load()
+    assert capi.timer_start(0) == capi.GQA_ERR_INVALID_ARG
+    assert capi.timer_start(-3) == capi.GQA_ERR_INVALID_ARG
+    st, ms, n = capi.timer_stop()
+    assert st == capi.GQA_ERR_INVALID_ARG and "no timing window" in capi.last_error()
+    assert lib.gqa_attn_timer_stop(None, None) == capi.GQA_ERR_INVALID_ARG

@@ -321,3 +321,45 @@ def test_split_kv_plans_no_records():
     assert n > rows * heads * 2 * D * 4
     assert (n - 256) % (rows * heads * (D * 4 + 8)) == 0  # partials of S slices, no records
     parity.compare(c, parity.run_gpu(c))
+
+
+@pytest.mark.parametrize("kind", ["prefill_split", "decode"])
+def test_main_kernel_timer(kind):
+    # the library's main-kernel timing window: one event pair per call
+    # around the attention kernel (the merge / combine kernels outside),
+    # calls past the window's size not timed, outputs unchanged; the timed
+    # kernel fits inside the whole call that torch's events measure
+    rng = np.random.default_rng(7760)
+    if kind == "prefill_split":
+        ql = rng.integers(1, 60, size=8)
+        kl = ql + rng.integers(3000, 6000, size=8)
+        c = synth.generate(seed=7760, q_lens=ql, kv_lens=kl, num_heads=32, kv_num_heads=8,
+                           head_dim=128, query_form="packed_nhd", kv_form="padded_bhnd",
+                           dtype=torch.bfloat16, n_kv=int(kl.max()) + 3,
+                           causal_kind="lower_right", device=DEV, name="timer-prefill")
+    else:
+        kl = rng.integers(100, 20000, size=16)
+        c = synth.generate(seed=7761, q_lens=np.ones(16, int), kv_lens=kl, num_heads=32,
+                           kv_num_heads=8, head_dim=128, n_q=1, n_kv=int(kl.max()) + 5,
+                           dtype=torch.float16, pass_query_lengths=False, device=DEV,
+                           name="timer-decode")
+    ref = parity.run_gpu(c)
+    assert capi.timer_start(2) == capi.GQA_OK
+    assert capi.timer_start(2) == capi.GQA_ERR_INVALID_ARG  # one window at a time
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    outs = []
+    s.record()
+    for _ in range(3):
+        o = synth.sentinel_like(c.q.shape, c.out_dtype, c.q.device)
+        outs.append(capi.attn_forward(c.q, c.k, c.v, c.mask, out=o, **c.kwargs()))
+    e.record()
+    torch.cuda.synchronize()
+    st, ms, n = capi.timer_stop()
+    assert st == capi.GQA_OK, capi.last_error()
+    assert n == 2  # the third call is past the window
+    whole = s.elapsed_time(e) / 3
+    assert 0 < ms / n <= whole * 1.05, (ms / n, whole)
+    for o in outs:
+        assert torch.equal(o, ref)
+    st, _, _ = capi.timer_stop()
+    assert st == capi.GQA_ERR_INVALID_ARG  # closed
