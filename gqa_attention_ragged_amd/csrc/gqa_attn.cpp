@@ -852,12 +852,14 @@ int gqa_attn_timer_start(int max_launches) {
     if (t.on.load()) return fail(GQA_ERR_INVALID_ARG, "a timing window is already open");
     t.ev.assign(2 * (size_t)max_launches, nullptr);
     for (size_t i = 0; i < t.ev.size(); ++i) {
-        const hipError_t e = hipEventCreate(&t.ev[i]);
+        // timing-only events: no system-scope fence when they complete (its
+        // cache writeback would be timed with the kernel and slow the next one)
+        const hipError_t e = hipEventCreateWithFlags(&t.ev[i], hipEventDisableSystemFence);
         if (e != hipSuccess) {
             t.ev.resize(i);
             destroy_events(t);
             g_hip_err = (int)e;
-            return fail(GQA_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+            return fail(GQA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
         }
     }
     t.used = 0;
