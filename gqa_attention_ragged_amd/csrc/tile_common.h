@@ -10,11 +10,21 @@ namespace gqa {
 
 // V is staged row-major; the 16-byte units of row `key` are XOR-swizzled so
 // that the transpose reads of one instruction (8 keys x 64 bytes for 16-bit
-// V, 16 keys x 32 bytes for fp8 V) spread evenly over the LDS banks.
+// V, 16 keys x 32 bytes for fp8 V) spread evenly over the LDS banks.  An fp8
+// read's half-wave covers keys base + {0..3, 8..11} (key bits 0, 1 and 3) and
+// one pair of units in each row; rows that share a 256-byte bank line differ
+// in the key bits below RPL, so the swizzle takes the remaining ones (bits 1
+// and 3 with two rows per line, bit 3 with four) to give the rows at one
+// line position disjoint unit pairs.
 template <typename C>
 __device__ __forceinline__ int v_swz(int key) {
-    if constexpr (C::FP8) return 2 * ((key / C::RPL) % (C::VUNITS / 2));
-    else return 4 * ((key / C::RPL) % (C::VUNITS / 4));
+    if constexpr (C::FP8) {
+        static_assert(C::RPL == 2 || C::RPL == 4, "fp8 V rows of 128 or 64 bytes");
+        if constexpr (C::RPL == 2) return 2 * (((key >> 1) & 1) | (((key >> 3) & 1) << 1));
+        else return 2 * ((key >> 3) & 1);
+    } else {
+        return 4 * ((key / C::RPL) % (C::VUNITS / 4));
+    }
 }
 // Byte offset of element d of V row `key`.
 template <typename C>
