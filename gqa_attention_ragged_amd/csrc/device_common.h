@@ -57,6 +57,8 @@ struct AttnParams {
     float* part_ml;                   // [B, Hq, S, 2]
     int32_t split_keys, n_splits;
     int32_t xcds;                     // >1: prefill workgroups remapped over this many XCDs
+    int32_t mirror;                   // prefill grid of one round: second half of the
+                                      // heaviest-first positions taken in reverse
     const int32_t* tree;              // draft-token parents, token-aligned with Q's rows, or null
     // paged KV: k / v are page pools [P, H_kv, 2^page_shift, D]; ptab is the
     // page table [B, 2, ptab_pages] (K pages, then V pages, per sequence)

@@ -702,6 +702,10 @@ int forward_planned(const gqa_attn_args_t* args, Plan& plan, void* workspace,
                 const int n_wg = plan.grid_x * plan.grid_y * std::max(plan.p.n_splits, 1);
                 e = gqa::launch_prefill_plan(plan.p, (int32_t*)plan.p.wrec, n_wg, s);
             }
+            // one round of workgroups (two per CU): heavy and light work
+            // items share the CUs (the kernel's in-grid map)
+            const int64_t n_wg = (int64_t)plan.grid_x * plan.grid_y * std::max(plan.p.n_splits, 1);
+            plan.p.mirror = !recs && n_wg <= 2 * (int64_t)device_cus();
             if (e == hipSuccess)
                 e = gqa::launch_prefill(plan.p, plan.q_elem, plan.head_dim, plan.grid_x,
                                         plan.grid_y, s);

@@ -1030,6 +1030,12 @@ struct Prefill {
             int bx = blockIdx.x, by = blockIdx.y;
             bz = blockIdx.z;
             if (p.xcds > 1) xcd_remap(p.xcds, gridDim.x, gridDim.y, gridDim.z, bx, by, bz);
+            // A grid of one round (a slot for every workgroup): an XCD hands
+            // its workgroups to its CUs round-robin, so in heaviest-first
+            // order the two workgroups of a CU were of similar weight; the
+            // second half of the positions, reversed, pairs the heaviest
+            // with the lightest (tree decoding +4%).
+            if (p.mirror && bx >= (int)gridDim.x / 2) bx = gridDim.x - 1 - (bx - (int)gridDim.x / 2);
             // dispatch position -> (sequence, row tile), heaviest first
             map_tile(p, bx, R, s_map, si);
             b = __builtin_amdgcn_readfirstlane(s_map[0]);
