@@ -29,14 +29,21 @@ thread_local int g_hip_err = 0;
 
 // Main-kernel timing window (gqa_attn_timer_start / _stop): event pairs
 // recorded around the main kernel of each call while the window is open.
+// A call reserves its pair when it records the first event and closes it
+// with the second (the reservation is per thread and per window, so calls
+// on several threads never mix their pairs).
 struct MainTimer {
     std::atomic<bool> on{false};
     std::mutex mu;
     std::vector<hipEvent_t> ev;  // pair i: ev[2i] before, ev[2i + 1] after
-    int used = 0;                // pairs recorded
-    bool pending = false;        // ev[2 * used] recorded, its partner not yet
+    std::vector<char> done;      // pair i has both events recorded
+    int next = 0;                // pairs reserved
+    unsigned gen = 0;            // window number
     hipError_t err = hipSuccess;
 };
+// this thread's open pair: (window number, pair index), index < 0: none
+thread_local unsigned t_pair_gen = 0;
+thread_local int t_pair = -1;
 MainTimer& main_timer() {
     static MainTimer t;
     return t;
@@ -563,23 +570,29 @@ int plan_call(const gqa_attn_args_t* a, Plan* plan) {
 
 namespace gqa {
 void main_kernel_begin(hipStream_t stream) {
+    t_pair = -1;
     MainTimer& t = main_timer();
     if (!t.on.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> g(t.mu);
-    if (!t.on.load(std::memory_order_relaxed) || 2 * t.used >= (int)t.ev.size()) return;
-    const hipError_t e = hipEventRecord(t.ev[2 * t.used], stream);
-    if (e != hipSuccess) t.err = e;
-    t.pending = e == hipSuccess;
+    if (!t.on.load(std::memory_order_relaxed) || 2 * t.next >= (int)t.ev.size()) return;
+    const hipError_t e = hipEventRecord(t.ev[2 * t.next], stream);
+    if (e != hipSuccess) {
+        t.err = e;
+        return;
+    }
+    t_pair = t.next++;
+    t_pair_gen = t.gen;
 }
 void main_kernel_end(hipStream_t stream) {
+    const int i = t_pair;
+    t_pair = -1;
+    if (i < 0) return;
     MainTimer& t = main_timer();
-    if (!t.on.load(std::memory_order_acquire)) return;
     std::lock_guard<std::mutex> g(t.mu);
-    if (!t.pending) return;
-    const hipError_t e = hipEventRecord(t.ev[2 * t.used + 1], stream);
+    if (!t.on.load(std::memory_order_relaxed) || t_pair_gen != t.gen) return;  // window closed
+    const hipError_t e = hipEventRecord(t.ev[2 * i + 1], stream);
     if (e != hipSuccess) t.err = e;
-    else ++t.used;
-    t.pending = false;
+    else t.done[i] = 1;
 }
 }  // namespace gqa
 
@@ -866,8 +879,9 @@ int gqa_attn_timer_start(int max_launches) {
             return fail(GQA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
         }
     }
-    t.used = 0;
-    t.pending = false;
+    t.done.assign((size_t)max_launches, 0);
+    t.next = 0;
+    ++t.gen;
     t.err = hipSuccess;
     t.on.store(true, std::memory_order_release);
     return GQA_OK;
@@ -881,16 +895,18 @@ int gqa_attn_timer_stop(double* total_ms, int* launches) {
     t.on.store(false, std::memory_order_release);
     hipError_t e = t.err;
     double sum = 0.0;
-    for (int i = 0; i < t.used && e == hipSuccess; ++i) {
+    int n = 0;
+    for (int i = 0; i < t.next && e == hipSuccess; ++i) {
+        if (!t.done[i]) continue;  // a call still between its two records
         e = hipEventSynchronize(t.ev[2 * i + 1]);
         float ms = 0.f;
         if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev[2 * i], t.ev[2 * i + 1]);
         sum += ms;
+        ++n;
     }
-    const int n = t.used;
     destroy_events(t);
-    t.used = 0;
-    t.pending = false;
+    t.done.clear();
+    t.next = 0;
     if (e != hipSuccess) {
         g_hip_err = (int)e;
         return fail(GQA_ERR_HIP, "main-kernel timing: %s", hipGetErrorString(e));

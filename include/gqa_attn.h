@@ -261,9 +261,10 @@ int gqa_attn_check_lengths(const gqa_attn_args_t* args, const int32_t* query_len
  * events and closes the window.  Errors: GQA_ERR_INVALID_ARG (max_launches
  * <= 0, a window already open or none open, a null output pointer),
  * GQA_ERR_HIP (creating, recording or timing the events failed; the window
- * is closed).  One window per process, shared by all threads (its records
- * are serialized by the library).  Not for calls under graph capture (the
- * event records would be captured with them). */
+ * is closed).  One window per process, shared by all threads: each call's
+ * pair belongs to the calling thread, and a call still between its two
+ * records when the window closes is not counted.  Not for calls under graph
+ * capture (the event records would be captured with them). */
 int gqa_attn_timer_start(int max_launches);
 int gqa_attn_timer_stop(double* total_ms, int* launches);
 

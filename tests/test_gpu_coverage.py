@@ -363,3 +363,48 @@ def test_main_kernel_timer(kind):
         assert torch.equal(o, ref)
     st, _, _ = capi.timer_stop()
     assert st == capi.GQA_ERR_INVALID_ARG  # closed
+
+
+def test_main_kernel_timer_two_threads():
+    # two threads, each on its own stream, call the library while one timing
+    # window is open: every call's pair is its own (6 timed calls), and the
+    # outputs are those of an untimed call
+    import threading
+    rng = np.random.default_rng(7770)
+    ql = rng.integers(1, 200, size=6)
+    kl = ql + rng.integers(0, 900, size=6)
+    c = synth.generate(seed=7770, q_lens=ql, kv_lens=kl, num_heads=8, kv_num_heads=2,
+                       head_dim=128, query_form="packed_nhd", kv_form="packed_nhd",
+                       dtype=torch.float16, causal_kind="lower_right", device=DEV,
+                       name="timer-threads")
+    ref = parity.run_gpu(c)
+    outs, errors = {}, []
+
+    def work(k):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                res = []
+                for _ in range(3):
+                    o = synth.sentinel_like(c.q.shape, c.out_dtype, c.q.device)
+                    res.append(capi.attn_forward(c.q, c.k, c.v, c.mask, out=o, **c.kwargs()))
+                stream.synchronize()
+            outs[k] = res
+        except Exception as e:  # surfaced below
+            errors.append(e)
+
+    torch.cuda.synchronize()
+    assert capi.timer_start(10) == capi.GQA_OK
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    st, ms, n = capi.timer_stop()
+    assert not errors, errors
+    assert st == capi.GQA_OK, capi.last_error()
+    assert n == 6 and ms > 0
+    for k in range(2):
+        for o in outs[k]:
+            assert torch.equal(o, ref)
